@@ -1,0 +1,379 @@
+#!/usr/bin/env python3
+"""Throughput of the fixed-order fold on one MI355X.
+
+Headline workload: fold_ranks over a stacked [8][16777216] float32 arena
+(64 MiB per slot), slot r = vecf(2^24, 1000 + r), into a separate output.
+One step is one fold_ranks call; it moves (W+1)*len*4 = 603,979,776 bytes
+(W slots read, one output written).  The inputs are resident in HBM before
+the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+prints one JSON line: metric, value (GB/s of algorithmic bytes), the roofline
+of the fold kernel, the CPU oracle timed on the host as a reported baseline,
+and the 16 KiB in-place fold latency.  Other modes (not the headline):
+
+    --workload {w8,w4,w16,join}   other configurations, same JSON shape
+    --sweep                       launch-geometry sweep of the headline fold
+    --copy-calibration            a plain device copy of known size, for
+                                  scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+METRIC = "fold GB/s (W+1 bufs moved) and % HBM peak at W=8, 64 MiB/slot; 16 KiB latency"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fold_w8_64mib_hbm_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "deterministic_fixed_order_amd", "csrc", "detfold.hip")
+
+WORKLOADS = {
+    # name: (family, W, len, seed0, scaled inv_w or None, base offset in elements)
+    "w8": ("vecf", 8, 1 << 24, 1000, None, 0),
+    "w4": ("mixed", 4, 100_000_000, 2000, 0.25, 0),
+    "w16": ("vecf", 16, 10_000_019, 3000, None, 1),
+}
+WORKLOAD_NAMES = {
+    "w8": "fold_ranks W=8 stacked [8][16777216] f32 (64 MiB/slot), uniform [-1,1)",
+    "w4": "fold_ranks_scaled W=4 stacked [4][100000000] f32, mixed magnitudes, inv_w=0.25",
+    "w16": "fold_ranks W=16 stacked [16][10000019] f32 at base+1 element, uniform [-1,1)",
+    "join": "fold_into n=4096 f32 (16 KiB per buffer)",
+}
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_counters():
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        text = open(COUNTERS_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
+
+
+class Timer:
+    """HIP events on the stream the fold is launched on (timing enabled)."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def region(self, fn, reps: int) -> float:
+        torch = self.torch
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(self.stream)
+        for _ in range(reps):
+            fn()
+        end.record(self.stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)  # ms
+
+
+def make_workload(name, torch, dev, want_host=False):
+    import numpy as np
+    import fold_inputs
+
+    family, W, n, seed0, inv_w, offset = WORKLOADS[name]
+    host = fold_inputs.slots(family, W, n, seed0)
+    alloc = torch.empty(W * n + offset, dtype=torch.float32, device=dev)
+    stacked = alloc[offset:].view(W, n)
+    stacked.copy_(torch.from_numpy(host))
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    return host, stacked, out, W, n, inv_w
+
+
+def bench_fold(args, torch, df, dev):
+    import numpy as np
+
+    name = args.workload
+    host, stacked, out, W, n, inv_w = make_workload(name, torch, dev)
+    bytes_per_step = (W + 1) * n * 4
+    stream = torch.cuda.current_stream(dev)
+    timer = Timer(torch, stream)
+    if inv_w is None:
+        def step():
+            df.fold_ranks(out, stacked)
+    else:
+        def step():
+            df.fold_ranks_scaled(out, stacked, inv_w)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done (%d steps); timing %d steps of %s" % (args.warmup, args.steps, name))
+    ms_total = timer.region(step, args.steps)
+    ms_per_step = ms_total / args.steps
+    gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    log("timed region: %.3f ms per step, %.1f GB/s" % (ms_per_step, gbs))
+
+    # per-launch event pairs, each call preceded by a 1 GiB scrub write so the
+    # 256 MB last-level cache holds none of the operands when the fold starts
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    singles = []
+    for i in range(args.singles):
+        scrub.fill_(float(i))
+        singles.append(timer.region(step, 1))
+    del scrub
+    log("single launches after a cache scrub: median %.3f ms, best %.3f ms"
+        % (statistics.median(singles), min(singles)))
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded xorshift64 generators, resident in HBM)",
+        "config": {"workload": WORKLOAD_NAMES[name], "W": W, "len": n,
+                   "bytes_per_step": bytes_per_step, "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+    }
+    counters = read_counters() if name == "w8" else None
+    traffic = None
+    if counters:
+        traffic = counters.get("hbm_bytes_per_launch")
+    result["roofline"] = {
+        "bound": "hbm",
+        "achieved": round(gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
+        "algorithmic_bytes_per_launch": bytes_per_step,
+        "avg_launch_ms": round(ms_per_step, 6),
+    }
+    result["scrubbed_single_launch"] = {
+        "median_ms": round(statistics.median(singles), 6),
+        "best_ms": round(min(singles), 6),
+        "median_GBps": round(bytes_per_step / (statistics.median(singles) * 1e-3) / 1e9, 2),
+        "calls": len(singles),
+        "note": "event pair per call, 1 GiB scrub write before each",
+    }
+    if args.workload == "w8" and not args.no_latency:
+        result["latency_16KiB"] = bench_join(args, torch, df, dev, timer)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step)
+    return result
+
+
+def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
+    """Name of the kernel instance the default launch uses (from the host plan)."""
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
+    body = "k_fold_vector" if p["path"] == df.PATH_VECTOR else "k_fold_scalar"
+    ws = W if W in (1, 2, 4, 8, 16) else 0
+    return "%s<%d,%d,%s> grid=%d block=%d" % (body, ws, p["unroll"], str(scaled).lower(),
+                                               p["grid"], p["block"])
+
+
+def bench_join(args, torch, df, dev, timer):
+    """In-place fold of two 16 KiB buffers (n = 4096): back-to-back per-call
+    time, and host-observed enqueue-to-complete time of single calls."""
+    import fold_inputs
+
+    n = 4096
+    xa = torch.from_numpy(fold_inputs.vecf(n, 11 + n)).to(dev)
+    stage = torch.from_numpy(fold_inputs.vecf(n, 77 + n)).to(dev)
+    one_a = torch.zeros(1, dtype=torch.float32, device=dev)
+    one_b = torch.zeros(1, dtype=torch.float32, device=dev)
+    for _ in range(50):
+        df.fold_into(xa, stage)
+    torch.cuda.synchronize()
+    reps = 1000
+    b2b = timer.region(lambda: df.fold_into(xa, stage), reps) / reps
+    floor = timer.region(lambda: df.fold_into(one_a, one_b), reps) / reps
+    host_us = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        df.fold_into(xa, stage)
+        torch.cuda.current_stream(dev).synchronize()
+        host_us.append((time.perf_counter() - t0) * 1e6)
+    return {
+        "n": n,
+        "bytes_per_call": 3 * 4 * n,
+        "back_to_back_us_per_call": round(b2b * 1e3, 3),
+        "one_element_back_to_back_us_per_call": round(floor * 1e3, 3),
+        "host_enqueue_to_complete_us_median": round(statistics.median(host_us), 3),
+        "calls": reps,
+    }
+
+
+def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
+    """The CPU oracle on the same host arrays, single-threaded, repeated for a
+    bounded time; its result is also checked bit for bit against the GPU's."""
+    import numpy as np
+    import torch
+    import oracle
+
+    fn = (lambda: oracle.fold_stacked(host)) if inv_w is None else \
+        (lambda: oracle.fold_stacked_scaled(host, np.float32(inv_w)))
+    want = fn()
+    times = []
+    t_start = time.perf_counter()
+    while (time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3) and len(times) < 200:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bit_exact = bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
+    log("cpu oracle: %d runs, median %.3f s (%.2f GB/s); GPU output bit-exact: %s"
+        % (len(times), med, bytes_per_step / med / 1e9, bit_exact))
+    return {
+        "value": round(bytes_per_step / med / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "the full workload arena (%d x %d f32), %d runs, median" % (W, n, len(times)),
+        "cpu_model": cpu_model(),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "gpu_output_bit_exact_vs_oracle": bit_exact,
+    }
+
+
+def bench_join_only(args, torch, df, dev):
+    timer = Timer(torch, torch.cuda.current_stream(dev))
+    lat = bench_join(args, torch, df, dev, timer)
+    n = lat["n"]
+    us = lat["back_to_back_us_per_call"]
+    return {
+        "metric": "16 KiB in-place fold latency (back-to-back)",
+        "value": us, "unit": "us/call", "n_gpus": 1, "steps": lat["calls"], "warmup": 50,
+        "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES["join"], "n": n}, "latency_16KiB": lat,
+    }
+
+
+def sweep(args, torch, df, dev):
+    """Launch-geometry sweep of the headline fold (all results bit-checked
+    against the default launch's output)."""
+    import numpy as np
+
+    host, stacked, out, W, n, _ = make_workload("w8", torch, dev)
+    timer = Timer(torch, torch.cuda.current_stream(dev))
+    df.fold_ranks(out, stacked)
+    ref = out.cpu().numpy().view(np.uint32).copy()
+    bytes_per_step = (W + 1) * n * 4
+    rows = []
+    for block in (128, 256, 512, 1024):
+        for unroll in (1, 2):
+            for grid in (0, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+                if grid and grid * block * unroll > 4 * (n // 4):
+                    continue
+
+                def step():
+                    df.fold_ranks_ex(out, stacked, block=block, grid=grid, unroll=unroll)
+                for _ in range(3):
+                    step()
+                ms = timer.region(step, 20) / 20
+                ok = np.array_equal(out.cpu().numpy().view(np.uint32), ref)
+                gbs = bytes_per_step / (ms * 1e-3) / 1e9
+                rows.append({"block": block, "unroll": unroll, "grid": grid, "ms": round(ms, 5),
+                             "GBps": round(gbs, 1), "bit_exact": ok})
+                log("sweep block=%4d unroll=%d grid=%6d: %.4f ms %.1f GB/s %s"
+                    % (block, unroll, grid, ms, gbs, "ok" if ok else "MISMATCH"))
+    return {"sweep": rows, "workload": WORKLOAD_NAMES["w8"]}
+
+
+def copy_calibration(args, torch, dev):
+    """A plain device-to-device copy of a known 256 MiB, for calibrating the
+    HBM byte counters (FETCH_SIZE should read the bytes copied, WRITE_SIZE the
+    bytes written)."""
+    nbytes = 256 << 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    timer = Timer(torch, torch.cuda.current_stream(dev))
+    ms = timer.region(lambda: dst.copy_(src), args.steps) / args.steps
+    return {"copy_calibration_bytes": nbytes, "ms_per_copy": round(ms, 5),
+            "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join"], default="w8")
+    ap.add_argument("--singles", type=int, default=30, help="scrubbed single-launch samples")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fold runs on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import __graft_entry__
+
+    __graft_entry__.ensure_built()
+    import deterministic_fixed_order_amd as df
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        res = copy_calibration(args, torch, dev)
+    elif args.sweep:
+        res = sweep(args, torch, df, dev)
+    elif args.workload == "join":
+        res = bench_join_only(args, torch, df, dev)
+    else:
+        res = bench_fold(args, torch, df, dev)
+    res["kernel_source_sha256_16"] = kernel_source_hash()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

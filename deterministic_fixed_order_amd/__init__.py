@@ -1,0 +1,198 @@
+"""Deterministic fixed-order fold on AMD Instinct MI355X -- Python binding.
+
+A thin ctypes layer over ``libdetfold.so`` (C ABI in ``include/detfold.h``).
+It only marshals arguments: it checks tensor dtype, device, shape and
+contiguity, passes raw device pointers and the caller's current HIP stream,
+and raises on a nonzero return code.  Every step of the fold runs in the HIP
+kernels; there is no CPU fallback, and importing a function whose library is
+missing raises.
+
+PyTorch is used for device memory and streams only.
+
+    fold_ranks(out, stacked)                 out = s_0 + s_1 + ... + s_{W-1}, ascending
+    fold_ranks_scaled(out, stacked, inv_w)   the same, then * inv_w
+    fold_into(dst, stage)                    dst = dst + stage (in place)
+
+``stacked`` is a ``[W, len]`` float32 CUDA/HIP tensor (row r = slot r); a view
+with a storage offset is fine as long as it is contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdetfold.so")
+
+OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_VECTOR, PATH_SCALAR = 0, 1, 2
+
+EXPORTS = (
+    "fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror", "detfold_abi_version",
+    "detfold_shard_plan", "detfold_plan_fold_ranks", "detfold_plan_fold_into",
+    "detfold_fold_ranks_ex",
+)
+
+
+class DetfoldError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        self.rc = rc
+        super().__init__("%s: detfold rc=%d (%s)" % (what, rc, strerror(rc)))
+
+
+class Launch(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("unroll", ctypes.c_int32), ("head", ctypes.c_int32), ("tail", ctypes.c_int32),
+                ("body", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libdetfold.so``; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libdetfold.so is not built at %s; run `python -c 'import __graft_entry__ as g; "
+            "g.build()'` from the repository root" % path)
+    lib = ctypes.CDLL(path)
+    vp, f32p, i32, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.fold_ranks.argtypes = [f32p, f32p, i32, i64, vp]
+    lib.fold_into.argtypes = [f32p, f32p, i64, vp]
+    lib.fold_ranks_scaled.argtypes = [f32p, f32p, i32, i64, ctypes.c_float, vp]
+    lib.detfold_fold_ranks_ex.argtypes = [f32p, f32p, i32, i64, i32, ctypes.c_float,
+                                          ctypes.POINTER(Launch), vp]
+    lib.detfold_strerror.argtypes = [ctypes.c_int]
+    lib.detfold_strerror.restype = ctypes.c_char_p
+    lib.detfold_abi_version.argtypes = []
+    lib.detfold_shard_plan.argtypes = [i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    # uintptr_t addresses: size_t has the same width on the supported hosts
+    lib.detfold_plan_fold_ranks.argtypes = [ctypes.c_size_t, ctypes.c_size_t, i32, i64, i32,
+                                            ctypes.POINTER(Launch), ctypes.POINTER(Plan)]
+    lib.detfold_plan_fold_into.argtypes = [ctypes.c_size_t, ctypes.c_size_t, i64, i32,
+                                           ctypes.POINTER(Plan)]
+    for name in ("fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_fold_ranks_ex",
+                 "detfold_abi_version", "detfold_shard_plan", "detfold_plan_fold_ranks",
+                 "detfold_plan_fold_into"):
+        getattr(lib, name).restype = ctypes.c_int
+    if lib.detfold_abi_version() != 1:
+        raise RuntimeError("libdetfold ABI mismatch")
+    _lib = lib
+    return lib
+
+
+def strerror(rc: int) -> str:
+    return load().detfold_strerror(rc).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise DetfoldError(rc, what)
+
+
+def _stream_handle(t, stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return int(s.cuda_stream)
+
+
+def _f32_device(t, name: str) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stacked_shape(out, stacked):
+    _f32_device(out, "out")
+    _f32_device(stacked, "stacked")
+    if stacked.dim() != 2:
+        raise ValueError("stacked must be [W, len], got shape %s" % (tuple(stacked.shape),))
+    W, n = stacked.shape
+    if out.numel() != n:
+        raise ValueError("out has %d elements, stacked rows have %d" % (out.numel(), n))
+    if out.device != stacked.device:
+        raise ValueError("out and stacked are on different devices")
+    return int(W), int(n)
+
+
+def fold_ranks(out, stacked, stream=None) -> None:
+    """``out[i] = ((stacked[0,i] + stacked[1,i]) + ...) + stacked[W-1,i]``."""
+    W, n = _stacked_shape(out, stacked)
+    _check(load().fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n,
+                             _stream_handle(out, stream)), "fold_ranks")
+
+
+def fold_ranks_scaled(out, stacked, inv_w: float, stream=None) -> None:
+    """``fold_ranks`` followed by one binary32 multiply of each sum by ``inv_w``."""
+    W, n = _stacked_shape(out, stacked)
+    _check(load().fold_ranks_scaled(out.data_ptr(), stacked.data_ptr(), W, n, float(inv_w),
+                                    _stream_handle(out, stream)), "fold_ranks_scaled")
+
+
+def fold_into(dst, stage, stream=None) -> None:
+    """``dst[i] = dst[i] + stage[i]`` in place."""
+    _f32_device(dst, "dst")
+    _f32_device(stage, "stage")
+    if dst.numel() != stage.numel():
+        raise ValueError("dst has %d elements, stage %d" % (dst.numel(), stage.numel()))
+    if dst.device != stage.device:
+        raise ValueError("dst and stage are on different devices")
+    _check(load().fold_into(dst.data_ptr(), stage.data_ptr(), dst.numel(),
+                            _stream_handle(dst, stream)), "fold_into")
+
+
+def fold_ranks_ex(out, stacked, *, scaled: bool = False, inv_w: float = 1.0, path: int = 0,
+                  block: int = 0, grid: int = 0, unroll: int = 0, stream=None) -> None:
+    """``fold_ranks`` / ``fold_ranks_scaled`` with an explicit launch override
+    (tests and tuning sweeps only)."""
+    W, n = _stacked_shape(out, stacked)
+    cfg = Launch(path, block, grid, unroll)
+    _check(load().detfold_fold_ranks_ex(out.data_ptr(), stacked.data_ptr(), W, n, int(scaled),
+                                        float(inv_w), ctypes.byref(cfg),
+                                        _stream_handle(out, stream)), "detfold_fold_ranks_ex")
+
+
+def shard_plan(n: int, world: int) -> list[tuple[int, int]]:
+    """Contiguous owner shards ``[(start, len), ...]`` of ``[0, n)``."""
+    if world < 1:
+        raise DetfoldError(EINVAL, "shard_plan")
+    start = (ctypes.c_int64 * world)()
+    length = (ctypes.c_int64 * world)()
+    _check(load().detfold_shard_plan(n, world, start, length), "shard_plan")
+    return [(start[p], length[p]) for p in range(world)]
+
+
+def plan_fold_ranks(out_addr: int, stacked_addr: int, W: int, n: int, cu_count: int,
+                    launch: Optional[dict] = None) -> dict:
+    """The plan ``fold_ranks`` would use (host only; addresses are integers)."""
+    p = Plan()
+    cfg = ctypes.byref(Launch(**launch)) if launch else None
+    _check(load().detfold_plan_fold_ranks(out_addr, stacked_addr, W, n, cu_count, cfg,
+                                          ctypes.byref(p)), "plan_fold_ranks")
+    return p.as_dict()
+
+
+def plan_fold_into(dst_addr: int, stage_addr: int, n: int, cu_count: int) -> dict:
+    """The plan ``fold_into`` would use (host only)."""
+    p = Plan()
+    _check(load().detfold_plan_fold_into(dst_addr, stage_addr, n, cu_count, ctypes.byref(p)),
+           "plan_fold_into")
+    return p.as_dict()

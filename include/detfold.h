@@ -1,0 +1,180 @@
+/*
+ * detfold.h -- deterministic fixed-order fold of float32 partial buffers on
+ * AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation (mamba-rs src/dist/reducer.rs: module note on the
+ * ReduceContract::FixedOrder contract, the `det_sum_ranks` kernel source and
+ * the host function `reduce_sum_reference`): W partial buffers s_0 .. s_{W-1}
+ * of `len` float32 values are combined elementwise as
+ *
+ *     acc = s_0[i];  acc = acc + s_r[i]  for r = 1 .. W-1, strictly ascending;
+ *
+ * every "+" a single IEEE 754 binary32 addition, round-to-nearest-even, with
+ * subnormals kept and no fused multiply-add.  The association order is fixed by
+ * program text, never by launch geometry, scheduling or memory layout, so the
+ * result is bit-identical to a host serial add chain of the same addends.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named as device pointers address memory of the calling thread's
+ *     current HIP device; `stream` is a hipStream_t of that device passed as
+ *     void* (NULL = the null stream).
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no
+ *     pointer after it returns, and does not synchronize: work is enqueued on
+ *     `stream` and the call returns.  Faults inside the kernels surface at the
+ *     caller's next synchronization of that stream.
+ *   - Float pointers must be 4-byte aligned; any 4-byte alignment is accepted
+ *     (misaligned or ragged lengths take a scalar path, never an error).
+ *   - A call with zero elements returns DETFOLD_OK and launches nothing
+ *     (mamba-rs src/dist/reducer.rs, `DetReduceKernel::launch`).
+ *   - Every entry point validates its arguments before any HIP call, so an
+ *     argument error never touches the device.
+ *   - The library keeps one piece of state: a per-device cache of the compute
+ *     unit count, filled on first use.  All entry points are thread-safe;
+ *     calls that write overlapping memory race as any two kernels would.
+ */
+#ifndef DETFOLD_H
+#define DETFOLD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  Only "0 = ok" is fixed by the pages (memra-engine
+ * tests/tp_ar_gpu.rs, `memra_tp_ar_fold` returns 0 on success); the others
+ * name the failure classes the pages describe as errors. */
+#define DETFOLD_OK 0       /* work enqueued (or nothing to do)                           */
+#define DETFOLD_EINVAL 1   /* W < 1, negative length, NULL or misaligned pointer with     */
+                           /* len > 0, size overflow, or an invalid launch override      */
+#define DETFOLD_EOVERLAP 2 /* output range overlaps an input range it must not alias     */
+#define DETFOLD_ELAUNCH 3  /* the HIP launch was refused                                 */
+#define DETFOLD_EDEVICE 4  /* no current HIP device, or its properties could not be read */
+
+/*
+ * fold_ranks -- out[i] = ((s_0[i] + s_1[i]) + ...) + s_{W-1}[i]
+ *
+ * Stacked arena layout (mamba-rs src/dist/reducer.rs, `det_sum_ranks` and
+ * `reduce_sum_fixed_order_nccl`): `stacked` is row-major [W][len], slot r
+ * (the addend from source rank r) at stacked + r*len.  `out` holds len floats.
+ *   out      device pointer, written (len floats)
+ *   stacked  device pointer, read (W*len floats)
+ *   W        number of addend slots, >= 1 (W = 1 copies slot 0 bit for bit)
+ *   len      elements per slot, >= 0 (64-bit; W*len*4 bytes must fit int64)
+ *   stream   hipStream_t of the current device
+ * Errors: DETFOLD_EINVAL, DETFOLD_EOVERLAP when [out, out+len) intersects
+ * [stacked, stacked+W*len) (the launch contract requires the regions not to
+ * overlap), DETFOLD_EDEVICE, DETFOLD_ELAUNCH.
+ */
+int fold_ranks(float *out, const float *stacked, int32_t W, int64_t len, void *stream);
+
+/*
+ * fold_into -- dst[i] = dst[i] + stage[i]   (in place; the two-addend fold)
+ *
+ * The decode-join fold of memra-engine tests/tp_ar_gpu.rs (C-ABI
+ * `memra_tp_ar_fold(dst, stage, n, stream)`): dst holds this rank's partial
+ * (slot 0), stage the peer's partial (slot 1).  Small payloads (16-256 KiB)
+ * take a latency path: a small grid, no device-side flags and no waits of any
+ * kind, so the fold completes whatever else is resident on the device (the
+ * page's note on the flag-spinning first cut that deadlocked on one card).
+ *   dst    device pointer, read and written (n floats)
+ *   stage  device pointer, read (n floats)
+ *   n      elements, >= 0
+ * Errors: DETFOLD_EINVAL, DETFOLD_EOVERLAP when the two ranges intersect,
+ * DETFOLD_EDEVICE, DETFOLD_ELAUNCH.
+ */
+int fold_into(float *dst, const float *stage, int64_t n, void *stream);
+
+/*
+ * fold_ranks_scaled -- out[i] = fold_ranks(...)[i] * inv_w
+ *
+ * The mean scale applied after the sum, as one binary32 multiply of the
+ * finished sum (mamba-rs src/dist/reducer.rs module note: the kernel forms the
+ * sum and the caller's 1/W scale follows it, exact for power-of-two W).  The
+ * scale is the caller's: inv_w is not checked against W, and any value
+ * (including non-powers of two) is applied as given.
+ * Arguments and errors as fold_ranks.
+ */
+int fold_ranks_scaled(float *out, const float *stacked, int32_t W, int64_t len, float inv_w,
+                      void *stream);
+
+/* Static, NUL-terminated description of a return code (never NULL). */
+const char *detfold_strerror(int rc);
+
+/* ABI revision of this header; bumped on any incompatible change. */
+#define DETFOLD_ABI_VERSION 1
+int detfold_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Owner shards (host only; no device access).
+ *
+ * detfold_shard_plan -- split [0, n) into `world` contiguous owner shards, as
+ * the transport dataflow does before each owner folds its own shard
+ * (mamba-rs src/dist/reducer.rs, `shard_plan` as used by
+ * `reduce_sum_fixed_order_nccl` and `LoopbackWorld::run_round`; the split
+ * itself is not printed there).  Balanced split: shard p has
+ * n/world + (p < n%world) elements, shards in ascending order, so a shard may
+ * be empty when n < world.  The fold's bits do not depend on the split.
+ *   start, length  host arrays of `world` int64, written
+ * Errors: DETFOLD_EINVAL for world < 1, n < 0 or NULL arrays.
+ */
+int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length);
+
+/* ------------------------------------------------------------------------
+ * Launch planning and the test-only launch override.
+ *
+ * The kernels read each slot with 16-byte loads when `out` and every slot sit
+ * at the same offset modulo 16 bytes (a "vector" body with up to 3 scalar
+ * elements before it and up to 3 after it); otherwise every element takes a
+ * coalesced 4-byte load ("scalar" body).  Either body computes the same
+ * per-element chain, so the path and the geometry never change a bit.
+ */
+#define DETFOLD_PATH_AUTO 0
+#define DETFOLD_PATH_VECTOR 1
+#define DETFOLD_PATH_SCALAR 2
+
+typedef struct detfold_launch {
+    int32_t path;   /* DETFOLD_PATH_*; VECTOR where the alignment forbids it is EINVAL */
+    int32_t block;  /* threads per workgroup: 0 = default, else a multiple of 64 in [64, 1024] */
+    int64_t grid;   /* workgroups: 0 = default, else >= 1 (a grid-stride loop covers the rest) */
+    int32_t unroll; /* groups (vector) or elements (scalar) per thread per pass: 0 = default, 1, 2 or 4 */
+} detfold_launch;
+
+typedef struct detfold_plan {
+    int32_t path;   /* DETFOLD_PATH_VECTOR or DETFOLD_PATH_SCALAR */
+    int32_t block;
+    int64_t grid;
+    int32_t unroll;
+    int32_t head;   /* scalar elements before the 16-byte-aligned body (vector path) */
+    int32_t tail;   /* scalar elements after it (vector path) */
+    int64_t body;   /* 4-element groups (vector path) or elements (scalar path) */
+} detfold_plan;
+
+/*
+ * detfold_plan_fold_ranks -- the path and geometry fold_ranks (and, with a
+ * launch override, detfold_fold_ranks_ex) would use for these addresses and
+ * sizes on a device with `cu_count` compute units.  Host only: addresses are
+ * plain integers and nothing is dereferenced.  `launch` may be NULL.
+ * Errors: as fold_ranks's argument checks, plus DETFOLD_EINVAL for a bad
+ * override or cu_count < 1.  With len == 0 the plan has grid = 0.
+ */
+int detfold_plan_fold_ranks(uintptr_t out, uintptr_t stacked, int32_t W, int64_t len,
+                            int32_t cu_count, const detfold_launch *launch, detfold_plan *plan);
+
+/* The plan fold_into would use (host only, as above). */
+int detfold_plan_fold_into(uintptr_t dst, uintptr_t stage, int64_t n, int32_t cu_count,
+                           detfold_plan *plan);
+
+/*
+ * detfold_fold_ranks_ex -- fold_ranks / fold_ranks_scaled with an explicit
+ * launch override.  For tests and tuning sweeps: it exists to show that the
+ * bits do not depend on path or geometry.  scaled = 0 ignores inv_w.
+ */
+int detfold_fold_ranks_ex(float *out, const float *stacked, int32_t W, int64_t len, int32_t scaled,
+                          float inv_w, const detfold_launch *launch, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETFOLD_H */

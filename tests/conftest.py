@@ -1,6 +1,8 @@
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -12,3 +14,29 @@ if TESTS not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP path through the C ABI")
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available() and torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    if any("gpu" in item.keywords for item in items) and not _gpu_present():
+        skip = pytest.mark.skip(reason="no GPU visible to torch")
+        for item in items:
+            if "gpu" in item.keywords:
+                item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def detfold_lib():
+    """The HIP library, built first if nothing is built yet."""
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import deterministic_fixed_order_amd as detfold
+    detfold.load()
+    return detfold

@@ -1,0 +1,209 @@
+"""Host-side checks of the C-ABI library (CPU only; nothing is launched).
+
+The library must load, export every function ``include/detfold.h`` declares,
+reject bad arguments before touching the device, and plan the path and
+geometry the kernels assume.  Every call here either fails validation or has
+nothing to do, so no fake address is ever handed to a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "detfold.h")
+
+KiB = 1024
+BASE = 0x7F0000000000  # a 4 KiB-aligned fake device address, never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(detfold_lib):
+    lib = detfold_lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), "libdetfold.so does not export %s" % name
+    assert set(detfold_lib.EXPORTS) == set(_declared_functions())
+
+
+def test_abi_version(detfold_lib):
+    assert detfold_lib.load().detfold_abi_version() == 1
+
+
+def test_strerror_covers_every_code(detfold_lib):
+    seen = set()
+    for rc in range(0, 5):
+        s = detfold_lib.strerror(rc)
+        assert s and s not in seen
+        seen.add(s)
+    assert "unknown" in detfold_lib.strerror(99)
+
+
+# --------------------------------------------------------------------------
+# argument validation happens before any HIP call
+
+def test_rejects_bad_arguments_without_a_device(detfold_lib):
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.OK
+    out, st = BASE, BASE + 64 * KiB * KiB
+    assert lib.fold_ranks(out, st, 0, 16, None) == EINVAL            # W = 0
+    assert lib.fold_ranks(out, st, -3, 16, None) == EINVAL
+    assert lib.fold_ranks(out, st, 4, -1, None) == EINVAL            # negative length
+    assert lib.fold_ranks(None, st, 4, 16, None) == EINVAL           # NULL
+    assert lib.fold_ranks(out, None, 4, 16, None) == EINVAL
+    assert lib.fold_ranks(out + 2, st, 4, 16, None) == EINVAL        # not 4-byte aligned
+    assert lib.fold_ranks(out, st + 1, 4, 16, None) == EINVAL
+    assert lib.fold_ranks(out, st, 4, (1 << 62), None) == EINVAL     # W*len*4 overflows
+    assert lib.fold_ranks(st + 8, st, 4, 16, None) == EOVERLAP       # out inside stacked
+    assert lib.fold_ranks(st - 4, st, 4, 16, None) == EOVERLAP       # out straddles the start
+    assert lib.fold_ranks(st + 4 * 64 - 4, st, 4, 16, None) == EOVERLAP  # last element
+    assert lib.fold_ranks_scaled(out, st, 0, 16, ctypes.c_float(0.5), None) == EINVAL
+    assert lib.fold_ranks_scaled(st, st, 2, 16, ctypes.c_float(0.5), None) == EOVERLAP
+    assert lib.fold_into(out, st, -1, None) == EINVAL
+    assert lib.fold_into(None, st, 8, None) == EINVAL
+    assert lib.fold_into(out, out + 16, 8, None) == EOVERLAP         # stage inside dst
+    assert lib.fold_into(out, out, 8, None) == EOVERLAP
+    # zero elements: nothing to do, no launch, even with NULL pointers
+    assert lib.fold_ranks(None, None, 8, 0, None) == OK
+    assert lib.fold_ranks_scaled(None, None, 1, 0, ctypes.c_float(1.0), None) == OK
+    assert lib.fold_into(None, None, 0, None) == OK
+    # W is still checked when there is nothing to fold
+    assert lib.fold_ranks(None, None, 0, 0, None) == EINVAL
+
+
+def test_rejects_bad_launch_overrides(detfold_lib):
+    lib = detfold_lib.load()
+    L = detfold_lib.Launch
+    out, st = BASE, BASE + 64 * KiB * KiB
+    for bad in (L(3, 0, 0, 0), L(-1, 0, 0, 0), L(0, 65, 0, 0), L(0, 32, 0, 0), L(0, 2048, 0, 0),
+                L(0, 0, -1, 0), L(0, 0, 1 << 40, 0), L(0, 0, 0, 3), L(0, 0, 0, 8)):
+        rc = lib.detfold_fold_ranks_ex(out, st, 8, 16, 0, ctypes.c_float(1.0), ctypes.byref(bad), None)
+        assert rc == detfold_lib.EINVAL
+        rc = lib.detfold_fold_ranks_ex(out, st, 8, 0, 0, ctypes.c_float(1.0), ctypes.byref(bad), None)
+        assert rc == detfold_lib.EINVAL, "a bad override is rejected even with nothing to fold"
+    # forcing the vector body where the slots are not co-aligned
+    vec = L(detfold_lib.PATH_VECTOR, 0, 0, 0)
+    rc = lib.detfold_fold_ranks_ex(out, st + 4, 8, 16, 0, ctypes.c_float(1.0), ctypes.byref(vec), None)
+    assert rc == detfold_lib.EINVAL
+
+
+# --------------------------------------------------------------------------
+# planning (pure host logic)
+
+CU = 256
+
+
+def test_plan_w8_64mib_per_slot(detfold_lib):
+    n = 1 << 24
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 8, n, CU)
+    assert p["path"] == detfold_lib.PATH_VECTOR
+    assert (p["head"], p["tail"], p["body"]) == (0, 0, n // 4)
+    assert p["block"] == 256 and p["unroll"] == 2
+    assert p["grid"] == min(-(-(n // 4) // (256 * 2)), CU * 8)
+
+
+def test_plan_w4_gradient_arena(detfold_lib):
+    n = 100_000_000
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 4, n, CU)
+    assert p["path"] == detfold_lib.PATH_VECTOR and p["body"] == n // 4 and p["tail"] == 0
+
+
+def test_plan_w16_offset_arena_is_scalar(detfold_lib):
+    n = 10_000_019
+    stacked = BASE + 4 * n + 4096 + 4  # one element past an aligned allocation
+    p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU)
+    assert p["path"] == detfold_lib.PATH_SCALAR and p["body"] == n
+    # slot phases cycle through all four offsets, so the vector body is illegal
+    phases = {((stacked + 4 * r * n) >> 2) & 3 for r in range(16)}
+    assert phases == {0, 1, 2, 3}
+
+
+@pytest.mark.parametrize("phase_out,phase_in,n", [(1, 1, 64), (2, 2, 4096), (3, 3, 8), (0, 0, 3),
+                                                   (1, 1, 2), (3, 3, 0)])
+def test_plan_head_and_tail(detfold_lib, phase_out, phase_in, n):
+    out = BASE + 4 * phase_out
+    st = BASE + (1 << 30) + 4 * phase_in
+    W = 4 if n % 4 == 0 else 1  # several slots share a phase only when len % 4 == 0
+    p = detfold_lib.plan_fold_ranks(out, st, W, n, CU)
+    assert p["path"] == detfold_lib.PATH_VECTOR
+    head = min((4 - phase_out) % 4, n)
+    assert p["head"] == head
+    assert p["body"] == (n - head) // 4 and p["tail"] == (n - head) % 4
+    assert p["head"] + 4 * p["body"] + p["tail"] == n
+    if n:
+        assert p["grid"] >= 1
+
+
+def test_plan_ragged_length_with_several_slots_is_scalar(detfold_lib):
+    # len % 4 != 0 puts slot 1 at another 16-byte phase than slot 0
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 2, 1001, CU)
+    assert p["path"] == detfold_lib.PATH_SCALAR
+    # one slot: only out and slot 0 matter
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 1, 1001, CU)
+    assert p["path"] == detfold_lib.PATH_VECTOR and p["tail"] == 1
+
+
+def test_plan_override(detfold_lib):
+    n = 1 << 20
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU,
+                                    dict(path=detfold_lib.PATH_SCALAR, block=1024, grid=7, unroll=4))
+    assert (p["path"], p["block"], p["grid"], p["unroll"]) == (detfold_lib.PATH_SCALAR, 1024, 7, 4)
+    assert p["body"] == n
+
+
+@pytest.mark.parametrize("n", [1, 4, 1024, 4096, 16384, 65536])
+def test_plan_decode_join_is_one_pass(detfold_lib, n):
+    p = detfold_lib.plan_fold_into(BASE, BASE + (1 << 20), n, CU)
+    assert p["unroll"] == 1
+    # every position gets its own thread: one pass, no grid-stride loop
+    assert p["grid"] * p["block"] >= p["body"]
+    assert p["grid"] == max(1, -(-p["body"] // p["block"]))
+    if n == 4096:
+        assert p["path"] == detfold_lib.PATH_VECTOR and p["grid"] == 4
+
+
+def test_plan_large_in_place_fold_streams(detfold_lib):
+    p = detfold_lib.plan_fold_into(BASE, BASE + (1 << 32), 100_000_000, CU)
+    assert p["grid"] == CU * 8 and p["unroll"] == 2
+
+
+# --------------------------------------------------------------------------
+# owner shards
+
+@pytest.mark.parametrize("n,world", [(10_000_019, 16), (0, 4), (3, 8), (16, 16), (1 << 24, 8), (7, 1)])
+def test_shard_plan_covers_contiguously_and_balanced(detfold_lib, n, world):
+    plan = detfold_lib.shard_plan(n, world)
+    assert len(plan) == world
+    pos = 0
+    for start, ln in plan:
+        assert start == pos and ln >= 0
+        pos += ln
+    assert pos == n
+    lens = [ln for _, ln in plan]
+    assert max(lens) - min(lens) <= 1
+    assert lens == sorted(lens, reverse=True)
+
+
+def test_shard_plan_for_the_offset_arena(detfold_lib):
+    lens = [ln for _, ln in detfold_lib.shard_plan(10_000_019, 16)]
+    assert lens == [625_002] * 3 + [625_001] * 13
+
+
+def test_shard_plan_rejects_bad_world(detfold_lib):
+    with pytest.raises(detfold_lib.DetfoldError):
+        detfold_lib.shard_plan(10, 0)
+    lib = detfold_lib.load()
+    a = (ctypes.c_int64 * 2)()
+    assert lib.detfold_shard_plan(-1, 2, a, a) == detfold_lib.EINVAL
+    assert lib.detfold_shard_plan(5, 2, None, a) == detfold_lib.EINVAL
