@@ -146,14 +146,15 @@ def bench_fold(args, torch, df, dev):
 
     # per-launch event pairs, each call preceded by a 1 GiB scrub write so the
     # 256 MB last-level cache holds none of the operands when the fold starts
-    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     singles = []
-    for i in range(args.singles):
-        scrub.fill_(float(i))
-        singles.append(timer.region(step, 1))
-    del scrub
-    log("single launches after a cache scrub: median %.3f ms, best %.3f ms"
-        % (statistics.median(singles), min(singles)))
+    if args.singles > 0:
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for i in range(args.singles):
+            scrub.fill_(float(i))
+            singles.append(timer.region(step, 1))
+        del scrub
+        log("single launches after a cache scrub: median %.3f ms, best %.3f ms"
+            % (statistics.median(singles), min(singles)))
 
     result = {
         "metric": METRIC,
@@ -187,13 +188,14 @@ def bench_fold(args, torch, df, dev):
         "algorithmic_bytes_per_launch": bytes_per_step,
         "avg_launch_ms": round(ms_per_step, 6),
     }
-    result["scrubbed_single_launch"] = {
-        "median_ms": round(statistics.median(singles), 6),
-        "best_ms": round(min(singles), 6),
-        "median_GBps": round(bytes_per_step / (statistics.median(singles) * 1e-3) / 1e9, 2),
-        "calls": len(singles),
-        "note": "event pair per call, 1 GiB scrub write before each",
-    }
+    if singles:
+        result["scrubbed_single_launch"] = {
+            "median_ms": round(statistics.median(singles), 6),
+            "best_ms": round(min(singles), 6),
+            "median_GBps": round(bytes_per_step / (statistics.median(singles) * 1e-3) / 1e9, 2),
+            "calls": len(singles),
+            "note": "event pair per call, 1 GiB scrub write before each",
+        }
     if args.workload == "w8" and not args.no_latency:
         result["latency_16KiB"] = bench_join(args, torch, df, dev, timer)
     if not args.no_cpu_baseline:
@@ -207,8 +209,9 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
     body = "k_fold_vector" if p["path"] == df.PATH_VECTOR else "k_fold_scalar"
     ws = W if W in (1, 2, 4, 8, 16) else 0
-    return "%s<%d,%d,%s> grid=%d block=%d" % (body, ws, p["unroll"], str(scaled).lower(),
-                                               p["grid"], p["block"])
+    pol = 1 if p["policy"] == df.POLICY_STREAM else 0
+    return "%s<%d,%d,%s,%d> grid=%d block=%d" % (body, ws, p["unroll"], str(scaled).lower(), pol,
+                                                  p["grid"], p["block"])
 
 
 def bench_join(args, torch, df, dev, timer):
@@ -301,24 +304,32 @@ def sweep(args, torch, df, dev):
     df.fold_ranks(out, stacked)
     ref = out.cpu().numpy().view(np.uint32).copy()
     bytes_per_step = (W + 1) * n * 4
-    rows = []
-    for block in (128, 256, 512, 1024):
-        for unroll in (1, 2):
-            for grid in (0, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
-                if grid and grid * block * unroll > 4 * (n // 4):
-                    continue
+    configs = []
+    for policy in (df.POLICY_STREAM, df.POLICY_CACHED):
+        for block in (128, 256, 512, 1024):
+            for unroll in ((1, 2) if policy == df.POLICY_STREAM else (1,)):
+                for grid in (0, 1024, 2048, 4096):
+                    configs.append((policy, block, unroll, grid))
+    samples = {c: [] for c in configs}
+    for rnd in range(3):  # interleaved rounds: drift affects every configuration alike
+        for c in configs:
+            policy, block, unroll, grid = c
 
-                def step():
-                    df.fold_ranks_ex(out, stacked, block=block, grid=grid, unroll=unroll)
-                for _ in range(3):
-                    step()
-                ms = timer.region(step, 20) / 20
-                ok = np.array_equal(out.cpu().numpy().view(np.uint32), ref)
-                gbs = bytes_per_step / (ms * 1e-3) / 1e9
-                rows.append({"block": block, "unroll": unroll, "grid": grid, "ms": round(ms, 5),
-                             "GBps": round(gbs, 1), "bit_exact": ok})
-                log("sweep block=%4d unroll=%d grid=%6d: %.4f ms %.1f GB/s %s"
-                    % (block, unroll, grid, ms, gbs, "ok" if ok else "MISMATCH"))
+            def step():
+                df.fold_ranks_ex(out, stacked, block=block, grid=grid, unroll=unroll, policy=policy)
+            for _ in range(3):
+                step()
+            samples[c].append(timer.region(step, 20) / 20)
+            if rnd == 0 and not np.array_equal(out.cpu().numpy().view(np.uint32), ref):
+                raise AssertionError("sweep configuration %s changed the bits" % (c,))
+    rows = []
+    for c in configs:
+        ms = statistics.median(samples[c])
+        gbs = bytes_per_step / (ms * 1e-3) / 1e9
+        rows.append({"policy": c[0], "block": c[1], "unroll": c[2], "grid": c[3],
+                     "ms": round(ms, 5), "GBps": round(gbs, 1), "bit_exact": True})
+        log("sweep policy=%d block=%4d unroll=%d grid=%5d: %.4f ms %.1f GB/s"
+            % (c[0], c[1], c[2], c[3], ms, gbs))
     return {"sweep": rows, "workload": WORKLOAD_NAMES["w8"]}
 
 

@@ -27,6 +27,8 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR = 0, 1, 2
+POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
+ABI_VERSION = 2
 
 EXPORTS = (
     "fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror", "detfold_abi_version",
@@ -43,13 +45,13 @@ class DetfoldError(RuntimeError):
 
 class Launch(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32)]
+                ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32), ("policy", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("unroll", ctypes.c_int32), ("head", ctypes.c_int32), ("tail", ctypes.c_int32),
-                ("body", ctypes.c_int64)]
+                ("policy", ctypes.c_int32), ("body", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -87,7 +89,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "detfold_abi_version", "detfold_shard_plan", "detfold_plan_fold_ranks",
                  "detfold_plan_fold_into"):
         getattr(lib, name).restype = ctypes.c_int
-    if lib.detfold_abi_version() != 1:
+    if lib.detfold_abi_version() != ABI_VERSION:
         raise RuntimeError("libdetfold ABI mismatch")
     _lib = lib
     return lib
@@ -160,11 +162,12 @@ def fold_into(dst, stage, stream=None) -> None:
 
 
 def fold_ranks_ex(out, stacked, *, scaled: bool = False, inv_w: float = 1.0, path: int = 0,
-                  block: int = 0, grid: int = 0, unroll: int = 0, stream=None) -> None:
+                  block: int = 0, grid: int = 0, unroll: int = 0, policy: int = 0,
+                  stream=None) -> None:
     """``fold_ranks`` / ``fold_ranks_scaled`` with an explicit launch override
     (tests and tuning sweeps only)."""
     W, n = _stacked_shape(out, stacked)
-    cfg = Launch(path, block, grid, unroll)
+    cfg = Launch(path, block, grid, unroll, policy)
     _check(load().detfold_fold_ranks_ex(out.data_ptr(), stacked.data_ptr(), W, n, int(scaled),
                                         float(inv_w), ctypes.byref(cfg),
                                         _stream_handle(out, stream)), "detfold_fold_ranks_ex")

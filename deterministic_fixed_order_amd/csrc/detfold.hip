@@ -40,104 +40,177 @@
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxBlock = 1024;
-constexpr int kDefaultBlock = 256;
-constexpr int kWorkgroupsPerCU = 8;  // default cap for the grid-stride grid
-constexpr int kLatencyBlock = 256;
-constexpr int kChunk = 8;            // slots loaded per batch when W is a runtime value
+constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth path
+constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
+
+// Memory policy of a launch.
+//  kStream  the bandwidth path: every input byte is read once, so loads carry
+//           the non-temporal hint, and stores are written through the
+//           per-XCD L2 (scope bits sc0 sc1) instead of sitting there dirty
+//           until an eviction competes with the incoming loads.
+//  kCached  the decode-join path: no hints; its output is read again soon.
+enum Policy : int { kCached = 0, kStream = 1 };
+
+// Cache-policy operand of the gfx950 buffer instructions: bit 0 = sc0,
+// bit 1 = nt, bit 4 = sc1.
+template <int POL> struct Aux {
+    static constexpr int load = POL == kStream ? 2 : 0;    // nt
+    static constexpr int store = POL == kStream ? 17 : 0;  // sc0 sc1
+};
+
+// Raw buffer descriptor word 3 for gfx9-family parts (32-bit data format,
+// no swizzle); the range check is num_records in bytes.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+template <int AUX> __device__ __forceinline__ void bload(f4 &v, __amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX));
+}
+template <int AUX> __device__ __forceinline__ void bload(float &v, __amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, AUX));
+}
+template <int AUX> __device__ __forceinline__ void bstore(f4 v, __amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), rs, off, 0, AUX);
+}
+template <int AUX> __device__ __forceinline__ void bstore(float v, __amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rs, off, 0, AUX);
+}
 
 // ---------------------------------------------------------------------------
 // Device side
 
-// Fold one tile: U independent positions (U groups of 4 elements, or U single
-// elements), each at offset off[u] of `out` and of every slot.  Slot 0 is s0,
-// slot r >= 1 is s1 + (r-1)*stride.  WS > 0 is a compile-time slot count; WS
-// == 0 reads it from w.
-template <int WS, int U, typename T, bool SCALED>
+// One tile of `cnt` positions (16-byte groups or single elements, T) starting
+// at position `start` of `out` and of every slot; slot 0 is s0, slot r >= 1 is
+// s1 + (r-1)*stride.  Thread tid owns positions tid + u*B for u < U.  Every
+// slot is read through a buffer descriptor based at the tile's start, so the
+// per-lane offsets are 32-bit however large the arena is.  GUARD: a partial
+// (last) tile, whose positions are checked against cnt.
+template <int WS, int U, typename T, bool SCALED, int POL, bool GUARD>
 __device__ __forceinline__ void fold_tile(T *out, const T *s0, const T *s1, int64_t stride, int w,
-                                          const int64_t (&off)[U], float inv_w)
+                                          int64_t start, int64_t cnt, float inv_w)
 {
+    const uint32_t B = blockDim.x;
+    const uint32_t bytes = (uint32_t)(cnt * (int64_t)sizeof(T));
+    uint32_t off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t p = threadIdx.x + (uint32_t)u * B;
+        off[u] = p * (uint32_t)sizeof(T);
+        ok[u] = !GUARD || (int64_t)p < cnt;
+    }
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + start, bytes);
     if constexpr (WS > 0) {
         T v[U][WS];
+        const __amdgpu_buffer_rsrc_t r0 = make_rsrc(s0 + start, bytes);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u][0] = s0[off[u]];
+            if (ok[u])
+                bload<Aux<POL>::load>(v[u][0], r0, off[u]);
 #pragma unroll
-        for (int r = 1; r < WS; ++r)
+        for (int r = 1; r < WS; ++r) {
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(s1 + (int64_t)(r - 1) * stride + start, bytes);
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                v[u][r] = s1[(int64_t)(r - 1) * stride + off[u]];
+                if (ok[u])
+                    bload<Aux<POL>::load>(v[u][r], rr, off[u]);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (!ok[u])
+                continue;
             T acc = v[u][0];
 #pragma unroll
             for (int r = 1; r < WS; ++r)
                 acc = acc + v[u][r];  // ascending slot order, one rounding per add
             if constexpr (SCALED)
                 acc = acc * inv_w;  // one rounding of the finished sum
-            out[off[u]] = acc;
+            bstore<Aux<POL>::store>(acc, ro, off[u]);
         }
     } else {
         T acc[U];
+        const __amdgpu_buffer_rsrc_t r0 = make_rsrc(s0 + start, bytes);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            acc[u] = s0[off[u]];
-        for (int r0 = 1; r0 < w; r0 += kChunk) {
+            if (ok[u])
+                bload<Aux<POL>::load>(acc[u], r0, off[u]);
+        for (int r0i = 1; r0i < w; r0i += kChunk) {
             T v[U][kChunk];
 #pragma unroll
-            for (int k = 0; k < kChunk; ++k)
-                if (r0 + k < w)
+            for (int k = 0; k < kChunk; ++k) {
+                if (r0i + k < w) {
+                    const __amdgpu_buffer_rsrc_t rr =
+                        make_rsrc(s1 + (int64_t)(r0i + k - 1) * stride + start, bytes);
 #pragma unroll
                     for (int u = 0; u < U; ++u)
-                        v[u][k] = s1[(int64_t)(r0 + k - 1) * stride + off[u]];
+                        if (ok[u])
+                            bload<Aux<POL>::load>(v[u][k], rr, off[u]);
+                }
+            }
 #pragma unroll
             for (int k = 0; k < kChunk; ++k)
-                if (r0 + k < w)
+                if (r0i + k < w)
 #pragma unroll
                     for (int u = 0; u < U; ++u)
-                        acc[u] = acc[u] + v[u][k];
+                        if (ok[u])
+                            acc[u] = acc[u] + v[u][k];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (!ok[u])
+                continue;
             T a = acc[u];
             if constexpr (SCALED)
                 a = a * inv_w;
-            out[off[u]] = a;
+            bstore<Aux<POL>::store>(a, ro, off[u]);
         }
     }
 }
 
-// Grid-stride over `n` positions, U per thread per pass; a pass whose last
-// position is in range needs no per-position guard.
-template <int WS, int U, typename T, bool SCALED>
-__device__ __forceinline__ void fold_span(T *out, const T *s0, const T *s1, int64_t stride, int w,
-                                          int64_t n, float inv_w)
+// Tiles of B*U positions over [0, n); block b takes tiles b, b + grid, ...
+// With the default one-pass grid every block takes exactly one tile.
+template <int WS, int U, typename T, bool SCALED, int POL>
+__device__ __forceinline__ void fold_tiles(T *out, const T *s0, const T *s1, int64_t stride, int w,
+                                           int64_t n, float inv_w)
 {
-    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t base = gid; base < n; base += nthreads * U) {
-        if (base + (int64_t)(U - 1) * nthreads < n) {
-            int64_t off[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                off[u] = base + (int64_t)u * nthreads;
-            fold_tile<WS, U, T, SCALED>(out, s0, s1, stride, w, off, inv_w);
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t one[1] = {base + (int64_t)u * nthreads};
-                if (one[0] < n)
-                    fold_tile<WS, 1, T, SCALED>(out, s0, s1, stride, w, one, inv_w);
-            }
-        }
+    const int64_t tile = (int64_t)blockDim.x * U;
+    for (int64_t start = (int64_t)blockIdx.x * tile; start < n; start += (int64_t)gridDim.x * tile) {
+        if (n - start >= tile)
+            fold_tile<WS, U, T, SCALED, POL, false>(out, s0, s1, stride, w, start, tile, inv_w);
+        else
+            fold_tile<WS, U, T, SCALED, POL, true>(out, s0, s1, stride, w, start, n - start, inv_w);
     }
+}
+
+// A single element with plain loads: the head and tail of the vector body.
+template <int WS, bool SCALED>
+__device__ __forceinline__ void fold_one(float *out, const float *s0, const float *s1,
+                                         int64_t stride, int w, int64_t i, float inv_w)
+{
+    const int nw = WS > 0 ? WS : w;
+    float acc = s0[i];
+    for (int r = 1; r < nw; ++r)
+        acc = acc + s1[(int64_t)(r - 1) * stride + i];
+    if constexpr (SCALED)
+        acc = acc * inv_w;
+    out[i] = acc;
 }
 
 // Vector body: elements [head, head + 4*groups) as 16-byte groups; the up to 3
 // elements before (head) and after (tail) are folded one by one by the first
 // threads of the grid.
-template <int WS, int U, bool SCALED>
+template <int WS, int U, bool SCALED, int POL>
 __global__ __launch_bounds__(kMaxBlock) void k_fold_vector(float *out, const float *s0,
                                                            const float *s1, int64_t stride, int w,
                                                            int64_t len, int64_t head, float inv_w)
@@ -146,23 +219,21 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_vector(float *out, const flo
     const int64_t tail0 = head + (groups << 2);
     const int64_t edges = head + (len - tail0);
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid < edges) {
-        const int64_t one[1] = {gid < head ? gid : tail0 + (gid - head)};
-        fold_tile<WS, 1, float, SCALED>(out, s0, s1, stride, w, one, inv_w);
-    }
-    fold_span<WS, U, f4, SCALED>(reinterpret_cast<f4 *>(out + head),
-                                 reinterpret_cast<const f4 *>(s0 + head),
-                                 reinterpret_cast<const f4 *>(s1 + head), stride >> 2, w, groups,
-                                 inv_w);
+    if (gid < edges)
+        fold_one<WS, SCALED>(out, s0, s1, stride, w, gid < head ? gid : tail0 + (gid - head), inv_w);
+    fold_tiles<WS, U, f4, SCALED, POL>(reinterpret_cast<f4 *>(out + head),
+                                       reinterpret_cast<const f4 *>(s0 + head),
+                                       reinterpret_cast<const f4 *>(s1 + head), stride >> 2, w,
+                                       groups, inv_w);
 }
 
 // Scalar body: every element with 4-byte loads (slots at mixed 16-byte phases).
-template <int WS, int U, bool SCALED>
+template <int WS, int U, bool SCALED, int POL>
 __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const float *s0,
                                                            const float *s1, int64_t stride, int w,
                                                            int64_t len, float inv_w)
 {
-    fold_span<WS, U, float, SCALED>(out, s0, s1, stride, w, len, inv_w);
+    fold_tiles<WS, U, float, SCALED, POL>(out, s0, s1, stride, w, len, inv_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -190,12 +261,11 @@ bool vector_legal(const Geometry &g)
     return true;
 }
 
-int default_unroll(int path, int32_t w)
-{
-    if (path == DETFOLD_PATH_VECTOR)
-        return w >= 16 || w == 0 ? 1 : 2;
-    return 4;
-}
+// Positions per thread per pass.  The vector body moves 16 bytes per slot per
+// position, and one position per thread keeps the most waves in flight (the
+// measured best on MI355X); the scalar body moves 4 bytes per slot per
+// position, so each thread takes four.
+int default_unroll(int path) { return path == DETFOLD_PATH_VECTOR ? 1 : 4; }
 
 int check_override(const detfold_launch *o)
 {
@@ -209,20 +279,31 @@ int check_override(const detfold_launch *o)
         return DETFOLD_EINVAL;
     if (o->unroll != 0 && o->unroll != 1 && o->unroll != 2 && o->unroll != 4)
         return DETFOLD_EINVAL;
+    if (o->policy < 0 || o->policy > DETFOLD_POLICY_CACHED)
+        return DETFOLD_EINVAL;
+    if (o->policy == DETFOLD_POLICY_CACHED && o->unroll > 1)
+        return DETFOLD_EINVAL;  // the unhinted kernels exist with unroll 1 only
     return DETFOLD_OK;
 }
 
-// Path and geometry for one call.  The default grid covers the body in one
-// pass when that takes at most cu_count * kWorkgroupsPerCU workgroups, and is
-// capped there otherwise (the grid-stride loop does the rest).
-int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, detfold_plan *p)
+// Path and geometry for one call.  Default geometry: one pass (each workgroup
+// folds one tile of block*unroll positions, so the grid is as large as the
+// body needs); the workgroup is kStreamBlock threads, halved (down to 64) while
+// that would leave compute units without a workgroup, so mid-size and small
+// folds still spread over the whole chip.  An override replaces any of path,
+// block, grid and unroll; a grid smaller than one pass makes the workgroups
+// loop over tiles.
+int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, int policy,
+              detfold_plan *p)
 {
     if (cu_count < 1)
         return DETFOLD_EINVAL;
     int rc = check_override(ovr);
     if (rc != DETFOLD_OK)
         return rc;
-    const detfold_launch o = ovr ? *ovr : detfold_launch{DETFOLD_PATH_AUTO, 0, 0, 0};
+    const detfold_launch o = ovr ? *ovr : detfold_launch{DETFOLD_PATH_AUTO, 0, 0, 0, 0};
+    if (o.policy)
+        policy = o.policy;
 
     const bool vec_ok = vector_legal(g);
     int path = o.path;
@@ -232,8 +313,8 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, de
         return DETFOLD_EINVAL;
 
     p->path = path;
-    p->block = o.block ? o.block : kDefaultBlock;
-    p->unroll = o.unroll ? o.unroll : default_unroll(path, g.w <= 16 ? g.w : 0);
+    p->policy = policy;
+    p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
     if (path == DETFOLD_PATH_VECTOR) {
         int64_t head = (4 - phase16(g.out)) & 3;
         if (head > g.len)
@@ -246,6 +327,13 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, de
         p->tail = 0;
         p->body = g.len;
     }
+    int block = o.block;
+    if (!block) {
+        block = kStreamBlock;
+        while (block > 64 && (p->body + (int64_t)block * p->unroll - 1) / ((int64_t)block * p->unroll) < cu_count)
+            block >>= 1;
+    }
+    p->block = block;
     if (g.len == 0) {
         p->grid = 0;
         return DETFOLD_OK;
@@ -254,8 +342,9 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, de
     int64_t need = (p->body + per_block - 1) / per_block;
     if (need < 1)
         need = 1;  // a body of zero groups still needs threads for head and tail
-    const int64_t cap = (int64_t)cu_count * kWorkgroupsPerCU;
-    p->grid = o.grid ? o.grid : (need < cap ? need : cap);
+    if (need > 0x7FFFFFFF)
+        need = 0x7FFFFFFF;  // the grid-stride loop covers the rest
+    p->grid = o.grid ? o.grid : need;
     return DETFOLD_OK;
 }
 
@@ -344,51 +433,56 @@ typedef void (*vector_kernel_t)(float *, const float *, const float *, int64_t, 
 typedef void (*scalar_kernel_t)(float *, const float *, const float *, int64_t, int, int64_t,
                                 float);
 
+// Kernel instances: compile-time slot counts for the common power-of-two
+// worlds (others use the runtime-W body, which loads slots in batches of
+// kChunk), unroll 1, 2 or 4 with streaming hints, unroll 1 without hints.
 template <int WS, bool SCALED>
-vector_kernel_t pick_vector_u(int unroll)
+vector_kernel_t pick_vector_w(int unroll, int policy)
 {
+    if (policy == kCached)
+        return k_fold_vector<WS, 1, SCALED, kCached>;
     switch (unroll) {
-    case 1: return k_fold_vector<WS, 1, SCALED>;
-    case 2: return k_fold_vector<WS, 2, SCALED>;
-    default: return k_fold_vector<WS, 4, SCALED>;
+    case 1: return k_fold_vector<WS, 1, SCALED, kStream>;
+    case 2: return k_fold_vector<WS, 2, SCALED, kStream>;
+    default: return k_fold_vector<WS, 4, SCALED, kStream>;
     }
 }
 
 template <int WS, bool SCALED>
-scalar_kernel_t pick_scalar_u(int unroll)
+scalar_kernel_t pick_scalar_w(int unroll, int policy)
 {
+    if (policy == kCached)
+        return k_fold_scalar<WS, 1, SCALED, kCached>;
     switch (unroll) {
-    case 1: return k_fold_scalar<WS, 1, SCALED>;
-    case 2: return k_fold_scalar<WS, 2, SCALED>;
-    default: return k_fold_scalar<WS, 4, SCALED>;
-    }
-}
-
-// Compile-time slot counts for the common power-of-two worlds; others use the
-// runtime-W body, which loads slots in batches of kChunk.
-template <bool SCALED>
-vector_kernel_t pick_vector(int32_t w, int unroll)
-{
-    switch (w) {
-    case 1: return pick_vector_u<1, SCALED>(unroll);
-    case 2: return pick_vector_u<2, SCALED>(unroll);
-    case 4: return pick_vector_u<4, SCALED>(unroll);
-    case 8: return pick_vector_u<8, SCALED>(unroll);
-    case 16: return pick_vector_u<16, SCALED>(unroll);
-    default: return pick_vector_u<0, SCALED>(unroll);
+    case 1: return k_fold_scalar<WS, 1, SCALED, kStream>;
+    case 2: return k_fold_scalar<WS, 2, SCALED, kStream>;
+    default: return k_fold_scalar<WS, 4, SCALED, kStream>;
     }
 }
 
 template <bool SCALED>
-scalar_kernel_t pick_scalar(int32_t w, int unroll)
+vector_kernel_t pick_vector(int32_t w, int unroll, int policy)
 {
     switch (w) {
-    case 1: return pick_scalar_u<1, SCALED>(unroll);
-    case 2: return pick_scalar_u<2, SCALED>(unroll);
-    case 4: return pick_scalar_u<4, SCALED>(unroll);
-    case 8: return pick_scalar_u<8, SCALED>(unroll);
-    case 16: return pick_scalar_u<16, SCALED>(unroll);
-    default: return pick_scalar_u<0, SCALED>(unroll);
+    case 1: return pick_vector_w<1, SCALED>(unroll, policy);
+    case 2: return pick_vector_w<2, SCALED>(unroll, policy);
+    case 4: return pick_vector_w<4, SCALED>(unroll, policy);
+    case 8: return pick_vector_w<8, SCALED>(unroll, policy);
+    case 16: return pick_vector_w<16, SCALED>(unroll, policy);
+    default: return pick_vector_w<0, SCALED>(unroll, policy);
+    }
+}
+
+template <bool SCALED>
+scalar_kernel_t pick_scalar(int32_t w, int unroll, int policy)
+{
+    switch (w) {
+    case 1: return pick_scalar_w<1, SCALED>(unroll, policy);
+    case 2: return pick_scalar_w<2, SCALED>(unroll, policy);
+    case 4: return pick_scalar_w<4, SCALED>(unroll, policy);
+    case 8: return pick_scalar_w<8, SCALED>(unroll, policy);
+    case 16: return pick_scalar_w<16, SCALED>(unroll, policy);
+    default: return pick_scalar_w<0, SCALED>(unroll, policy);
     }
 }
 
@@ -402,14 +496,17 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
     int w = g.w;
     int64_t len = g.len;
     int64_t head = p.head;
+    const int policy = p.policy == DETFOLD_POLICY_CACHED ? kCached : kStream;
     const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
     hipError_t e;
     if (p.path == DETFOLD_PATH_VECTOR) {
-        vector_kernel_t k = scaled ? pick_vector<true>(w, p.unroll) : pick_vector<false>(w, p.unroll);
+        vector_kernel_t k = scaled ? pick_vector<true>(w, p.unroll, policy)
+                                   : pick_vector<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
         e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
     } else {
-        scalar_kernel_t k = scaled ? pick_scalar<true>(w, p.unroll) : pick_scalar<false>(w, p.unroll);
+        scalar_kernel_t k = scaled ? pick_scalar<true>(w, p.unroll, policy)
+                                   : pick_scalar<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &inv_w};
         e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
     }
@@ -431,25 +528,22 @@ int run_ranks(float *out, const float *stacked, int32_t W, int64_t len, bool sca
     if ((rc = current_cu_count(&cu)) != DETFOLD_OK)
         return rc;
     detfold_plan p;
-    if ((rc = make_plan(g, cu, ovr, &p)) != DETFOLD_OK)
+    if ((rc = make_plan(g, cu, ovr, DETFOLD_POLICY_STREAM, &p)) != DETFOLD_OK)
         return rc;
     return launch_plan(g, p, scaled, inv_w, static_cast<hipStream_t>(stream));
 }
 
-// The decode-join path.  Payloads of 16-256 KiB are launch-latency bound:
-// one position per thread, one pass, a grid just large enough for that.  A
-// payload too large for one pass of cu_count * kWorkgroupsPerCU workgroups is
-// bandwidth bound and takes the default streaming plan instead.
+// The decode-join path.  Payloads up to kLatencyBytes per buffer are
+// launch-latency bound and their result is read again soon: one position per
+// thread, one pass, no cache hints.  Larger payloads are bandwidth bound and
+// take the streaming policy.
+constexpr int64_t kLatencyBytes = 8 << 20;
+
 int plan_into(const Geometry &g, int32_t cu_count, detfold_plan *p)
 {
-    const detfold_launch one_pass = {DETFOLD_PATH_AUTO, kLatencyBlock, 0, 1};
-    int rc = make_plan(g, cu_count, &one_pass, p);
-    if (rc != DETFOLD_OK || g.len == 0)
-        return rc;
-    const int64_t blocks = (p->body + kLatencyBlock - 1) / kLatencyBlock;
-    if (blocks <= (int64_t)cu_count * kWorkgroupsPerCU)
-        return DETFOLD_OK;  // make_plan's grid is already the one-pass grid
-    return make_plan(g, cu_count, nullptr, p);
+    const bool small = g.len * 4 <= kLatencyBytes;
+    const detfold_launch o = {DETFOLD_PATH_AUTO, 0, 0, 1, 0};
+    return make_plan(g, cu_count, &o, small ? DETFOLD_POLICY_CACHED : DETFOLD_POLICY_STREAM, p);
 }
 
 }  // namespace
@@ -530,7 +624,8 @@ int detfold_plan_fold_ranks(uintptr_t out, uintptr_t stacked, int32_t W, int64_t
                               reinterpret_cast<const float *>(stacked), W, len);
     if (rc != DETFOLD_OK)
         return rc;
-    return make_plan(ranks_geometry(out, stacked, W, len), cu_count, launch, plan);
+    return make_plan(ranks_geometry(out, stacked, W, len), cu_count, launch, DETFOLD_POLICY_STREAM,
+                     plan);
 }
 
 int detfold_plan_fold_into(uintptr_t dst, uintptr_t stage, int64_t n, int32_t cu_count,

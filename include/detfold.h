@@ -102,7 +102,7 @@ int fold_ranks_scaled(float *out, const float *stacked, int32_t W, int64_t len, 
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 1
+#define DETFOLD_ABI_VERSION 2
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -127,17 +127,28 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
  * at the same offset modulo 16 bytes (a "vector" body with up to 3 scalar
  * elements before it and up to 3 after it); otherwise every element takes a
  * coalesced 4-byte load ("scalar" body).  Either body computes the same
- * per-element chain, so the path and the geometry never change a bit.
+ * per-element chain, so the path, the geometry and the cache policy never
+ * change a bit.
+ *
+ * Cache policy: the bandwidth path (fold_ranks, fold_ranks_scaled, and
+ * fold_into above 8 MiB per buffer) streams: loads carry the non-temporal
+ * hint and stores are written through the L2.  fold_into at or below 8 MiB
+ * per buffer uses no hints, since the folded result is read again soon.
  */
 #define DETFOLD_PATH_AUTO 0
 #define DETFOLD_PATH_VECTOR 1
 #define DETFOLD_PATH_SCALAR 2
 
+#define DETFOLD_POLICY_DEFAULT 0
+#define DETFOLD_POLICY_STREAM 1 /* non-temporal loads, write-through stores */
+#define DETFOLD_POLICY_CACHED 2 /* no cache hints (available with unroll 1 only) */
+
 typedef struct detfold_launch {
     int32_t path;   /* DETFOLD_PATH_*; VECTOR where the alignment forbids it is EINVAL */
     int32_t block;  /* threads per workgroup: 0 = default, else a multiple of 64 in [64, 1024] */
-    int64_t grid;   /* workgroups: 0 = default, else >= 1 (a grid-stride loop covers the rest) */
-    int32_t unroll; /* groups (vector) or elements (scalar) per thread per pass: 0 = default, 1, 2 or 4 */
+    int64_t grid;   /* workgroups: 0 = one pass, else >= 1 (workgroups loop over the tiles) */
+    int32_t unroll; /* groups (vector) or elements (scalar) per thread per tile: 0 = default, 1, 2 or 4 */
+    int32_t policy; /* DETFOLD_POLICY_*: 0 = the entry point's own policy */
 } detfold_launch;
 
 typedef struct detfold_plan {
@@ -147,6 +158,7 @@ typedef struct detfold_plan {
     int32_t unroll;
     int32_t head;   /* scalar elements before the 16-byte-aligned body (vector path) */
     int32_t tail;   /* scalar elements after it (vector path) */
+    int32_t policy; /* DETFOLD_POLICY_STREAM or DETFOLD_POLICY_CACHED */
     int64_t body;   /* 4-element groups (vector path) or elements (scalar path) */
 } detfold_plan;
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == 1
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 2
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -86,14 +86,15 @@ def test_rejects_bad_launch_overrides(detfold_lib):
     lib = detfold_lib.load()
     L = detfold_lib.Launch
     out, st = BASE, BASE + 64 * KiB * KiB
-    for bad in (L(3, 0, 0, 0), L(-1, 0, 0, 0), L(0, 65, 0, 0), L(0, 32, 0, 0), L(0, 2048, 0, 0),
-                L(0, 0, -1, 0), L(0, 0, 1 << 40, 0), L(0, 0, 0, 3), L(0, 0, 0, 8)):
+    for bad in (L(3, 0, 0, 0, 0), L(-1, 0, 0, 0, 0), L(0, 65, 0, 0, 0), L(0, 32, 0, 0, 0),
+                L(0, 2048, 0, 0, 0), L(0, 0, -1, 0, 0), L(0, 0, 1 << 40, 0, 0), L(0, 0, 0, 3, 0),
+                L(0, 0, 0, 8, 0), L(0, 0, 0, 0, 3), L(0, 0, 0, 0, -1), L(0, 0, 0, 2, 2)):
         rc = lib.detfold_fold_ranks_ex(out, st, 8, 16, 0, ctypes.c_float(1.0), ctypes.byref(bad), None)
         assert rc == detfold_lib.EINVAL
         rc = lib.detfold_fold_ranks_ex(out, st, 8, 0, 0, ctypes.c_float(1.0), ctypes.byref(bad), None)
         assert rc == detfold_lib.EINVAL, "a bad override is rejected even with nothing to fold"
     # forcing the vector body where the slots are not co-aligned
-    vec = L(detfold_lib.PATH_VECTOR, 0, 0, 0)
+    vec = L(detfold_lib.PATH_VECTOR, 0, 0, 0, 0)
     rc = lib.detfold_fold_ranks_ex(out, st + 4, 8, 16, 0, ctypes.c_float(1.0), ctypes.byref(vec), None)
     assert rc == detfold_lib.EINVAL
 
@@ -109,8 +110,18 @@ def test_plan_w8_64mib_per_slot(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 8, n, CU)
     assert p["path"] == detfold_lib.PATH_VECTOR
     assert (p["head"], p["tail"], p["body"]) == (0, 0, n // 4)
-    assert p["block"] == 256 and p["unroll"] == 2
-    assert p["grid"] == min(-(-(n // 4) // (256 * 2)), CU * 8)
+    # one 16-byte group per thread, 512-thread workgroups, one pass
+    assert p["block"] == 512 and p["unroll"] == 1
+    assert p["grid"] == (n // 4) // 512 == 8192
+    assert p["policy"] == detfold_lib.POLICY_STREAM
+
+
+@pytest.mark.parametrize("n,block", [(1 << 20, 512), (1 << 19, 512), (1 << 18, 256), (1 << 16, 64),
+                                     (4096, 64), (4, 64)])
+def test_plan_block_shrinks_to_cover_the_chip(detfold_lib, n, block):
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU)
+    assert p["block"] == block
+    assert p["grid"] == max(1, -(-p["body"] // block))
 
 
 def test_plan_w4_gradient_arena(detfold_lib):
@@ -160,22 +171,27 @@ def test_plan_override(detfold_lib):
                                     dict(path=detfold_lib.PATH_SCALAR, block=1024, grid=7, unroll=4))
     assert (p["path"], p["block"], p["grid"], p["unroll"]) == (detfold_lib.PATH_SCALAR, 1024, 7, 4)
     assert p["body"] == n
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU,
+                                    dict(path=0, block=0, grid=0, unroll=0,
+                                         policy=detfold_lib.POLICY_CACHED))
+    assert p["policy"] == detfold_lib.POLICY_CACHED and p["unroll"] == 1
 
 
 @pytest.mark.parametrize("n", [1, 4, 1024, 4096, 16384, 65536])
 def test_plan_decode_join_is_one_pass(detfold_lib, n):
     p = detfold_lib.plan_fold_into(BASE, BASE + (1 << 20), n, CU)
-    assert p["unroll"] == 1
+    assert p["unroll"] == 1 and p["policy"] == detfold_lib.POLICY_CACHED
     # every position gets its own thread: one pass, no grid-stride loop
     assert p["grid"] * p["block"] >= p["body"]
     assert p["grid"] == max(1, -(-p["body"] // p["block"]))
     if n == 4096:
-        assert p["path"] == detfold_lib.PATH_VECTOR and p["grid"] == 4
+        assert p["path"] == detfold_lib.PATH_VECTOR and p["block"] == 64 and p["grid"] == 16
 
 
 def test_plan_large_in_place_fold_streams(detfold_lib):
     p = detfold_lib.plan_fold_into(BASE, BASE + (1 << 32), 100_000_000, CU)
-    assert p["grid"] == CU * 8 and p["unroll"] == 2
+    assert p["policy"] == detfold_lib.POLICY_STREAM and p["unroll"] == 1
+    assert p["block"] == 512 and p["grid"] == 25_000_000 // 512 + 1
 
 
 # --------------------------------------------------------------------------

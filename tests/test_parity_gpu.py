@@ -261,8 +261,9 @@ def test_w16_offset_arena_shards_equal_whole(env):
 # --------------------------------------------------------------------------
 # geometry and alignment: the bits never depend on them
 
-GEOMS = [dict(path=p, block=b, grid=g, unroll=u)
-         for p in (1, 2) for b in (64, 256, 1024) for g in (0, 1, 7) for u in (1, 2, 4)]
+GEOMS = [dict(path=p, block=b, grid=g, unroll=u, policy=pol)
+         for p in (1, 2) for b in (64, 256, 1024) for g in (0, 1, 7) for u in (1, 2, 4)
+         for pol in ((0, 2) if u == 1 else (0,))]
 
 
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 9, 16, 17, 24])
