@@ -207,6 +207,11 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     """Name of the kernel instance the default launch uses (from the host plan)."""
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
     p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
+    if p["path"] == df.PATH_ROWS:
+        aligned = (out.data_ptr() - stacked.data_ptr()) % 16 == 0 and (W <= 2 or n % 4 == 0) \
+            and (W < 2 or (out.data_ptr() - stacked.data_ptr() - 4 * n) % 16 == 0)
+        return "k_fold_rows<%d,%s,%s> grid=%d block=%d tile=%d" % (
+            W, str(aligned).lower(), str(scaled).lower(), p["grid"], p["block"], p["tile"])
     body = "k_fold_vector" if p["path"] == df.PATH_VECTOR else "k_fold_scalar"
     ws = W if W in (1, 2, 4, 8, 16) else 0
     pol = 1 if p["policy"] == df.POLICY_STREAM else 0
@@ -304,19 +309,20 @@ def sweep(args, torch, df, dev):
     df.fold_ranks(out, stacked)
     ref = out.cpu().numpy().view(np.uint32).copy()
     bytes_per_step = (W + 1) * n * 4
-    configs = []
+    configs = [(df.PATH_ROWS, df.POLICY_STREAM, 64 * W, 1, grid) for grid in (0, 512, 1024, 2048, 4096)]
     for policy in (df.POLICY_STREAM, df.POLICY_CACHED):
         for block in (128, 256, 512, 1024):
             for unroll in ((1, 2) if policy == df.POLICY_STREAM else (1,)):
                 for grid in (0, 1024, 2048, 4096):
-                    configs.append((policy, block, unroll, grid))
+                    configs.append((df.PATH_VECTOR, policy, block, unroll, grid))
     samples = {c: [] for c in configs}
     for rnd in range(3):  # interleaved rounds: drift affects every configuration alike
         for c in configs:
-            policy, block, unroll, grid = c
+            path, policy, block, unroll, grid = c
 
             def step():
-                df.fold_ranks_ex(out, stacked, block=block, grid=grid, unroll=unroll, policy=policy)
+                df.fold_ranks_ex(out, stacked, path=path, block=block, grid=grid, unroll=unroll,
+                                 policy=policy)
             for _ in range(3):
                 step()
             samples[c].append(timer.region(step, 20) / 20)
@@ -326,10 +332,10 @@ def sweep(args, torch, df, dev):
     for c in configs:
         ms = statistics.median(samples[c])
         gbs = bytes_per_step / (ms * 1e-3) / 1e9
-        rows.append({"policy": c[0], "block": c[1], "unroll": c[2], "grid": c[3],
+        rows.append({"path": c[0], "policy": c[1], "block": c[2], "unroll": c[3], "grid": c[4],
                      "ms": round(ms, 5), "GBps": round(gbs, 1), "bit_exact": True})
-        log("sweep policy=%d block=%4d unroll=%d grid=%5d: %.4f ms %.1f GB/s"
-            % (c[0], c[1], c[2], c[3], ms, gbs))
+        log("sweep path=%d policy=%d block=%4d unroll=%d grid=%5d: %.4f ms %.1f GB/s"
+            % (c[0], c[1], c[2], c[3], c[4], ms, gbs))
     return {"sweep": rows, "workload": WORKLOAD_NAMES["w8"]}
 
 

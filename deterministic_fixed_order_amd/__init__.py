@@ -26,9 +26,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdetfold.so")
 
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
-PATH_AUTO, PATH_VECTOR, PATH_SCALAR = 0, 1, 2
+PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTS = (
     "fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror", "detfold_abi_version",
@@ -51,7 +51,7 @@ class Launch(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("unroll", ctypes.c_int32), ("head", ctypes.c_int32), ("tail", ctypes.c_int32),
-                ("policy", ctypes.c_int32), ("body", ctypes.c_int64)]
+                ("policy", ctypes.c_int32), ("body", ctypes.c_int64), ("tile", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}

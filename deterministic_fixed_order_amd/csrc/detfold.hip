@@ -45,6 +45,14 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxBlock = 1024;
 constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth path
 constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
+constexpr int kMaxRowsW = 16;      // widest fold the LDS row body takes (one wave per slot)
+
+// KiB of one slot each wave of the LDS row body streams per tile: about
+// 64 KiB of LDS per workgroup (two workgroups per CU), 2..16 KiB per wave.
+constexpr int rows_kib_per_wave(int w)
+{
+    return 64 / w < 2 ? 2 : (64 / w > 16 ? 16 : 64 / w);
+}
 
 // Memory policy of a launch.
 //  kStream  the bandwidth path: every input byte is read once, so loads carry
@@ -236,6 +244,89 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
     fold_tiles<WS, U, float, SCALED, POL>(out, s0, s1, stride, w, len, inv_w);
 }
 
+// LDS row-transpose body (2 <= W <= 16).  One workgroup of W waves folds a
+// tile of T 16-byte groups of `out`: wave r streams the tile's bytes of slot r
+// -- LPW consecutive KiB, one contiguous run per wave -- straight into LDS row
+// r (buffer loads with the lds bit, no register staging); after a barrier
+// every thread folds whole groups from the W rows, in ascending row order, and
+// stores them.  Streaming one slot per wave keeps each wave on one run of HBM
+// rows; the direct body instead has every wave touch W runs 1 KiB at a time,
+// which measured 3-8% slower on MI355X.
+//
+// Slot phases: the tile of `out` starts 16-byte aligned; slot r's bytes for
+// the tile start delta_r = (phase(slot r) - phase(out)) mod 4 dwords past a
+// 16-byte boundary.  ALIGNED (every delta_r = 0): row r holds the tile
+// exactly.  Otherwise wave r loads the 16-byte blocks covering the tile's
+// bytes -- at most one block more, starting at most 12 bytes before them, and
+// never leaving the 16-byte blocks that hold the slot's first and last
+// elements -- and the fold reads each element at dword delta_r + 4t + k of
+// row r.  The bits are those of the per-element chain either way.
+template <int W> struct RowsShape {
+    static constexpr int LPW = rows_kib_per_wave(W);  // KiB each wave streams per tile
+    static constexpr int T = LPW * 64;                // 16-byte groups per tile
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int W, bool ALIGNED, bool SCALED>
+__global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, const float *s0, const float *s1,
+                                                      int64_t stride, int64_t len, int64_t head,
+                                                      float inv_w)
+{
+    constexpr int LPW = RowsShape<W>::LPW, T = RowsShape<W>::T;
+    constexpr int LOADS = ALIGNED ? LPW : LPW + 1;  // one more block when the slot is shifted
+    constexpr int ROW = LOADS * 64;                 // groups per LDS row
+    __shared__ f4 rows[W][ROW];
+
+    const int64_t groups = (len - head) >> 2;
+    const int64_t tail0 = head + (groups << 2);
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < head + (len - tail0))
+        fold_one<W, SCALED>(out, s0, s1, stride, W, gid < head ? gid : tail0 + (gid - head), inv_w);
+
+    const uint32_t lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const float *slot = r == 0 ? s0 : s1 + (int64_t)(r - 1) * stride;
+    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
+        const int64_t g0 = tile * T;
+        const int64_t cnt = groups - g0 < T ? groups - g0 : T;
+        const int64_t e0 = head + 4 * g0;  // first element of the tile; out + e0 is 16-byte aligned
+        const uintptr_t first = (uintptr_t)(slot + e0);
+        const uintptr_t lo = first & ~(uintptr_t)15;
+        const uintptr_t hi = ((uintptr_t)(slot + e0 + 4 * cnt) + 15) & ~(uintptr_t)15;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void *)lo, (uint32_t)(hi - lo));
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
+                                                     (uint32_t)(u * 64 + lane) * 16u, 0, 0,
+                                                     Aux<kStream>::load);
+        __syncthreads();  // every row has landed
+
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + e0, (uint32_t)(cnt * 16));
+        for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += W * 64) {
+            f4 acc;
+            if constexpr (ALIGNED) {
+                acc = rows[0][t];
+#pragma unroll
+                for (int q = 1; q < W; ++q)
+                    acc = acc + rows[q][t];  // ascending slot order, one rounding per add
+            } else {
+#pragma unroll
+                for (int q = 0; q < W; ++q) {
+                    const float *sq = q == 0 ? s0 : s1 + (int64_t)(q - 1) * stride;
+                    const uint32_t d = (uint32_t)(((uintptr_t)(sq + e0) >> 2) & 3);
+                    const float *row = reinterpret_cast<const float *>(&rows[q][0]) + d + 4 * t;
+                    const f4 v = {row[0], row[1], row[2], row[3]};
+                    acc = q == 0 ? v : acc + v;
+                }
+            }
+            if constexpr (SCALED)
+                acc = acc * inv_w;  // one rounding of the finished sum
+            bstore<Aux<kStream>::store>(acc, ro, t * 16u);
+        }
+        __syncthreads();  // the rows are refilled only after every thread has read them
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: planning (pure integer logic, no HIP calls)
 
@@ -271,7 +362,7 @@ int check_override(const detfold_launch *o)
 {
     if (!o)
         return DETFOLD_OK;
-    if (o->path < DETFOLD_PATH_AUTO || o->path > DETFOLD_PATH_SCALAR)
+    if (o->path < DETFOLD_PATH_AUTO || o->path > DETFOLD_PATH_ROWS)
         return DETFOLD_EINVAL;
     if (o->block != 0 && (o->block < 64 || o->block > kMaxBlock || (o->block % 64) != 0))
         return DETFOLD_EINVAL;
@@ -286,13 +377,15 @@ int check_override(const detfold_launch *o)
     return DETFOLD_OK;
 }
 
-// Path and geometry for one call.  Default geometry: one pass (each workgroup
-// folds one tile of block*unroll positions, so the grid is as large as the
-// body needs); the workgroup is kStreamBlock threads, halved (down to 64) while
-// that would leave compute units without a workgroup, so mid-size and small
-// folds still spread over the whole chip.  An override replaces any of path,
-// block, grid and unroll; a grid smaller than one pass makes the workgroups
-// loop over tiles.
+// Path and geometry for one call.
+//  * Streaming policy, 2 <= W <= 16: the LDS row body, one wave per slot
+//    (block = 64*W), one tile of 64*(64/W clamped to 2..16) groups per
+//    workgroup, one pass.
+//  * Otherwise the direct bodies: vector when `out` and every slot share a
+//    16-byte phase, else scalar; kStreamBlock threads, halved (down to 64)
+//    while that would leave compute units without a workgroup; one pass.
+// An override replaces any of path, block, grid, unroll and policy; a grid
+// smaller than one pass makes the workgroups loop over the tiles.
 int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, int policy,
               detfold_plan *p)
 {
@@ -306,44 +399,59 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
         policy = o.policy;
 
     const bool vec_ok = vector_legal(g);
+    const bool rows_ok = g.w >= 2 && g.w <= kMaxRowsW;
     int path = o.path;
-    if (path == DETFOLD_PATH_AUTO)
-        path = vec_ok ? DETFOLD_PATH_VECTOR : DETFOLD_PATH_SCALAR;
+    if (path == DETFOLD_PATH_AUTO) {
+        if (rows_ok && policy == DETFOLD_POLICY_STREAM)
+            path = DETFOLD_PATH_ROWS;
+        else
+            path = vec_ok ? DETFOLD_PATH_VECTOR : DETFOLD_PATH_SCALAR;
+    }
     if (path == DETFOLD_PATH_VECTOR && !vec_ok)
+        return DETFOLD_EINVAL;
+    if (path == DETFOLD_PATH_ROWS &&
+        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && o.block != 64 * g.w) || o.unroll > 1))
         return DETFOLD_EINVAL;
 
     p->path = path;
     p->policy = policy;
-    p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
-    if (path == DETFOLD_PATH_VECTOR) {
+    if (path == DETFOLD_PATH_SCALAR) {
+        p->head = 0;
+        p->tail = 0;
+        p->body = g.len;
+    } else {
         int64_t head = (4 - phase16(g.out)) & 3;
         if (head > g.len)
             head = g.len;
         p->head = (int32_t)head;
         p->body = (g.len - head) >> 2;
         p->tail = (int32_t)((g.len - head) & 3);
+    }
+    if (path == DETFOLD_PATH_ROWS) {
+        p->unroll = 1;
+        p->block = 64 * g.w;
+        p->tile = (int64_t)rows_kib_per_wave(g.w) * 64;
     } else {
-        p->head = 0;
-        p->tail = 0;
-        p->body = g.len;
+        p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
+        int block = o.block;
+        if (!block) {
+            block = kStreamBlock;
+            while (block > 64 &&
+                   (p->body + (int64_t)block * p->unroll - 1) / ((int64_t)block * p->unroll) < cu_count)
+                block >>= 1;
+        }
+        p->block = block;
+        p->tile = (int64_t)p->block * p->unroll;
     }
-    int block = o.block;
-    if (!block) {
-        block = kStreamBlock;
-        while (block > 64 && (p->body + (int64_t)block * p->unroll - 1) / ((int64_t)block * p->unroll) < cu_count)
-            block >>= 1;
-    }
-    p->block = block;
     if (g.len == 0) {
         p->grid = 0;
         return DETFOLD_OK;
     }
-    const int64_t per_block = (int64_t)p->block * p->unroll;
-    int64_t need = (p->body + per_block - 1) / per_block;
+    int64_t need = (p->body + p->tile - 1) / p->tile;
     if (need < 1)
         need = 1;  // a body of zero groups still needs threads for head and tail
     if (need > 0x7FFFFFFF)
-        need = 0x7FFFFFFF;  // the grid-stride loop covers the rest
+        need = 0x7FFFFFFF;  // the workgroups loop over the rest
     p->grid = o.grid ? o.grid : need;
     return DETFOLD_OK;
 }
@@ -460,6 +568,37 @@ scalar_kernel_t pick_scalar_w(int unroll, int policy)
     }
 }
 
+typedef void (*rows_kernel_t)(float *, const float *, const float *, int64_t, int64_t, int64_t,
+                              float);
+
+template <int W, bool SCALED>
+rows_kernel_t pick_rows_w(bool aligned)
+{
+    return aligned ? k_fold_rows<W, true, SCALED> : k_fold_rows<W, false, SCALED>;
+}
+
+template <bool SCALED>
+rows_kernel_t pick_rows(int32_t w, bool aligned)
+{
+    switch (w) {
+    case 2: return pick_rows_w<2, SCALED>(aligned);
+    case 3: return pick_rows_w<3, SCALED>(aligned);
+    case 4: return pick_rows_w<4, SCALED>(aligned);
+    case 5: return pick_rows_w<5, SCALED>(aligned);
+    case 6: return pick_rows_w<6, SCALED>(aligned);
+    case 7: return pick_rows_w<7, SCALED>(aligned);
+    case 8: return pick_rows_w<8, SCALED>(aligned);
+    case 9: return pick_rows_w<9, SCALED>(aligned);
+    case 10: return pick_rows_w<10, SCALED>(aligned);
+    case 11: return pick_rows_w<11, SCALED>(aligned);
+    case 12: return pick_rows_w<12, SCALED>(aligned);
+    case 13: return pick_rows_w<13, SCALED>(aligned);
+    case 14: return pick_rows_w<14, SCALED>(aligned);
+    case 15: return pick_rows_w<15, SCALED>(aligned);
+    default: return pick_rows_w<16, SCALED>(aligned);
+    }
+}
+
 template <bool SCALED>
 vector_kernel_t pick_vector(int32_t w, int unroll, int policy)
 {
@@ -499,7 +638,11 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
     const int policy = p.policy == DETFOLD_POLICY_CACHED ? kCached : kStream;
     const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
     hipError_t e;
-    if (p.path == DETFOLD_PATH_VECTOR) {
+    if (p.path == DETFOLD_PATH_ROWS) {
+        rows_kernel_t k = scaled ? pick_rows<true>(w, vector_legal(g)) : pick_rows<false>(w, vector_legal(g));
+        void *args[] = {&out, &s0, &s1, &stride, &len, &head, &inv_w};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
+    } else if (p.path == DETFOLD_PATH_VECTOR) {
         vector_kernel_t k = scaled ? pick_vector<true>(w, p.unroll, policy)
                                    : pick_vector<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
@@ -541,9 +684,11 @@ constexpr int64_t kLatencyBytes = 8 << 20;
 
 int plan_into(const Geometry &g, int32_t cu_count, detfold_plan *p)
 {
-    const bool small = g.len * 4 <= kLatencyBytes;
-    const detfold_launch o = {DETFOLD_PATH_AUTO, 0, 0, 1, 0};
-    return make_plan(g, cu_count, &o, small ? DETFOLD_POLICY_CACHED : DETFOLD_POLICY_STREAM, p);
+    if (g.len * 4 <= kLatencyBytes) {
+        const detfold_launch o = {DETFOLD_PATH_AUTO, 0, 0, 1, 0};
+        return make_plan(g, cu_count, &o, DETFOLD_POLICY_CACHED, p);
+    }
+    return make_plan(g, cu_count, nullptr, DETFOLD_POLICY_STREAM, p);
 }
 
 }  // namespace

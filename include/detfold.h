@@ -102,7 +102,7 @@ int fold_ranks_scaled(float *out, const float *stacked, int32_t W, int64_t len, 
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 2
+#define DETFOLD_ABI_VERSION 3
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -123,12 +123,19 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
 /* ------------------------------------------------------------------------
  * Launch planning and the test-only launch override.
  *
- * The kernels read each slot with 16-byte loads when `out` and every slot sit
- * at the same offset modulo 16 bytes (a "vector" body with up to 3 scalar
- * elements before it and up to 3 after it); otherwise every element takes a
- * coalesced 4-byte load ("scalar" body).  Either body computes the same
- * per-element chain, so the path, the geometry and the cache policy never
- * change a bit.
+ * Three bodies compute the same per-element chain, so the path, the geometry
+ * and the cache policy never change a bit:
+ *   ROWS    (default for 2 <= W <= 16 on the streaming policy) one workgroup of
+ *           W waves per tile; wave r streams a contiguous run of slot r into
+ *           LDS with 16-byte loads, realigning slots whose 16-byte phase
+ *           differs from out's; every thread then folds whole 16-byte groups
+ *           and stores them.  Up to 3 elements before the first 16-byte
+ *           boundary of `out` (head) and up to 3 after the last (tail) are
+ *           folded one by one.
+ *   VECTOR  (default for W = 1 or W > 16 when `out` and every slot share one
+ *           16-byte phase, and for the small in-place fold) each thread loads
+ *           16 bytes of every slot directly; head and tail as above.
+ *   SCALAR  (otherwise) each thread loads 4 bytes of every slot directly.
  *
  * Cache policy: the bandwidth path (fold_ranks, fold_ranks_scaled, and
  * fold_into above 8 MiB per buffer) streams: loads carry the non-temporal
@@ -136,8 +143,9 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
  * per buffer uses no hints, since the folded result is read again soon.
  */
 #define DETFOLD_PATH_AUTO 0
-#define DETFOLD_PATH_VECTOR 1
-#define DETFOLD_PATH_SCALAR 2
+#define DETFOLD_PATH_VECTOR 1 /* direct body, 16-byte loads (out and every slot co-aligned) */
+#define DETFOLD_PATH_SCALAR 2 /* direct body, 4-byte loads (any alignment)                 */
+#define DETFOLD_PATH_ROWS 3   /* LDS row body, 2 <= W <= 16, any alignment, streaming only  */
 
 #define DETFOLD_POLICY_DEFAULT 0
 #define DETFOLD_POLICY_STREAM 1 /* non-temporal loads, write-through stores */
@@ -145,21 +153,24 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
 
 typedef struct detfold_launch {
     int32_t path;   /* DETFOLD_PATH_*; VECTOR where the alignment forbids it is EINVAL */
-    int32_t block;  /* threads per workgroup: 0 = default, else a multiple of 64 in [64, 1024] */
+    int32_t block;  /* threads per workgroup: 0 = default, else a multiple of 64 in [64, 1024]
+                       (ROWS: 0 or 64*W) */
     int64_t grid;   /* workgroups: 0 = one pass, else >= 1 (workgroups loop over the tiles) */
-    int32_t unroll; /* groups (vector) or elements (scalar) per thread per tile: 0 = default, 1, 2 or 4 */
+    int32_t unroll; /* groups (vector) or elements (scalar) per thread per tile: 0 = default, 1, 2 or 4
+                       (ROWS: 0 or 1) */
     int32_t policy; /* DETFOLD_POLICY_*: 0 = the entry point's own policy */
 } detfold_launch;
 
 typedef struct detfold_plan {
-    int32_t path;   /* DETFOLD_PATH_VECTOR or DETFOLD_PATH_SCALAR */
+    int32_t path;   /* DETFOLD_PATH_ROWS, _VECTOR or _SCALAR */
     int32_t block;
     int64_t grid;
     int32_t unroll;
-    int32_t head;   /* scalar elements before the 16-byte-aligned body (vector path) */
-    int32_t tail;   /* scalar elements after it (vector path) */
+    int32_t head;   /* elements folded one by one before the 16-byte-aligned body (rows, vector) */
+    int32_t tail;   /* elements folded one by one after it (rows, vector) */
     int32_t policy; /* DETFOLD_POLICY_STREAM or DETFOLD_POLICY_CACHED */
-    int64_t body;   /* 4-element groups (vector path) or elements (scalar path) */
+    int64_t body;   /* 4-element groups (rows, vector) or elements (scalar) */
+    int64_t tile;   /* body positions one workgroup folds per pass */
 } detfold_plan;
 
 /*

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 2
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 3
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -86,7 +86,7 @@ def test_rejects_bad_launch_overrides(detfold_lib):
     lib = detfold_lib.load()
     L = detfold_lib.Launch
     out, st = BASE, BASE + 64 * KiB * KiB
-    for bad in (L(3, 0, 0, 0, 0), L(-1, 0, 0, 0, 0), L(0, 65, 0, 0, 0), L(0, 32, 0, 0, 0),
+    for bad in (L(4, 0, 0, 0, 0), L(-1, 0, 0, 0, 0), L(0, 65, 0, 0, 0), L(0, 32, 0, 0, 0),
                 L(0, 2048, 0, 0, 0), L(0, 0, -1, 0, 0), L(0, 0, 1 << 40, 0, 0), L(0, 0, 0, 3, 0),
                 L(0, 0, 0, 8, 0), L(0, 0, 0, 0, 3), L(0, 0, 0, 0, -1), L(0, 0, 0, 2, 2)):
         rc = lib.detfold_fold_ranks_ex(out, st, 8, 16, 0, ctypes.c_float(1.0), ctypes.byref(bad), None)
@@ -108,36 +108,59 @@ CU = 256
 def test_plan_w8_64mib_per_slot(detfold_lib):
     n = 1 << 24
     p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 8, n, CU)
-    assert p["path"] == detfold_lib.PATH_VECTOR
+    # LDS row body: one wave per slot, each streaming 8 KiB of its slot per tile
+    assert p["path"] == detfold_lib.PATH_ROWS
     assert (p["head"], p["tail"], p["body"]) == (0, 0, n // 4)
-    # one 16-byte group per thread, 512-thread workgroups, one pass
-    assert p["block"] == 512 and p["unroll"] == 1
+    assert p["block"] == 512 and p["tile"] == 512
     assert p["grid"] == (n // 4) // 512 == 8192
     assert p["policy"] == detfold_lib.POLICY_STREAM
 
 
+@pytest.mark.parametrize("W,kib", [(2, 16), (3, 16), (4, 16), (5, 12), (7, 9), (8, 8), (9, 7),
+                                   (13, 4), (16, 4)])
+def test_plan_rows_tile_per_width(detfold_lib, W, kib):
+    n = 1 << 22
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, n, CU)
+    assert p["path"] == detfold_lib.PATH_ROWS
+    assert p["block"] == 64 * W and p["tile"] == 64 * kib  # kib KiB of each slot per wave
+    assert p["grid"] == -(-(n // 4) // p["tile"])
+
+
+@pytest.mark.parametrize("W", [1, 17, 24])
 @pytest.mark.parametrize("n,block", [(1 << 20, 512), (1 << 19, 512), (1 << 18, 256), (1 << 16, 64),
                                      (4096, 64), (4, 64)])
-def test_plan_block_shrinks_to_cover_the_chip(detfold_lib, n, block):
-    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU)
-    assert p["block"] == block
+def test_plan_direct_block_shrinks_to_cover_the_chip(detfold_lib, W, n, block):
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, n, CU)
+    assert p["path"] == detfold_lib.PATH_VECTOR
+    assert p["block"] == block and p["tile"] == block
     assert p["grid"] == max(1, -(-p["body"] // block))
 
 
 def test_plan_w4_gradient_arena(detfold_lib):
     n = 100_000_000
     p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 4, n, CU)
-    assert p["path"] == detfold_lib.PATH_VECTOR and p["body"] == n // 4 and p["tail"] == 0
+    assert p["path"] == detfold_lib.PATH_ROWS and p["body"] == n // 4 and p["tail"] == 0
+    assert p["block"] == 256 and p["tile"] == 1024 and p["grid"] == -(-(n // 4) // 1024)
 
 
-def test_plan_w16_offset_arena_is_scalar(detfold_lib):
+def test_plan_w16_offset_arena(detfold_lib):
     n = 10_000_019
     stacked = BASE + 4 * n + 4096 + 4  # one element past an aligned allocation
-    p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU)
-    assert p["path"] == detfold_lib.PATH_SCALAR and p["body"] == n
-    # slot phases cycle through all four offsets, so the vector body is illegal
+    # slot phases cycle through all four offsets: no direct 16-byte body ...
     phases = {((stacked + 4 * r * n) >> 2) & 3 for r in range(16)}
     assert phases == {0, 1, 2, 3}
+    with pytest.raises(detfold_lib.DetfoldError):
+        detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU, dict(path=detfold_lib.PATH_VECTOR,
+                                                                   block=0, grid=0, unroll=0, policy=0))
+    # ... but the LDS row body realigns them: 16-byte groups of out, 3 tail elements
+    p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU)
+    assert p["path"] == detfold_lib.PATH_ROWS
+    assert (p["head"], p["body"], p["tail"]) == (0, n // 4, 3)
+    assert p["block"] == 1024 and p["tile"] == 256
+    # the direct scalar body stays available
+    p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU, dict(path=detfold_lib.PATH_SCALAR,
+                                                                   block=0, grid=0, unroll=0, policy=0))
+    assert p["path"] == detfold_lib.PATH_SCALAR and p["body"] == n
 
 
 @pytest.mark.parametrize("phase_out,phase_in,n", [(1, 1, 64), (2, 2, 4096), (3, 3, 8), (0, 0, 3),
@@ -147,7 +170,7 @@ def test_plan_head_and_tail(detfold_lib, phase_out, phase_in, n):
     st = BASE + (1 << 30) + 4 * phase_in
     W = 4 if n % 4 == 0 else 1  # several slots share a phase only when len % 4 == 0
     p = detfold_lib.plan_fold_ranks(out, st, W, n, CU)
-    assert p["path"] == detfold_lib.PATH_VECTOR
+    assert p["path"] == (detfold_lib.PATH_ROWS if W > 1 else detfold_lib.PATH_VECTOR)
     head = min((4 - phase_out) % 4, n)
     assert p["head"] == head
     assert p["body"] == (n - head) // 4 and p["tail"] == (n - head) % 4
@@ -156,9 +179,12 @@ def test_plan_head_and_tail(detfold_lib, phase_out, phase_in, n):
         assert p["grid"] >= 1
 
 
-def test_plan_ragged_length_with_several_slots_is_scalar(detfold_lib):
-    # len % 4 != 0 puts slot 1 at another 16-byte phase than slot 0
+def test_plan_ragged_length_with_several_slots(detfold_lib):
+    # len % 4 != 0 puts slot 1 at another 16-byte phase than slot 0: the row
+    # body realigns it, the direct bodies fall back to 4-byte loads
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 2, 1001, CU)
+    assert p["path"] == detfold_lib.PATH_ROWS and (p["body"], p["tail"]) == (250, 1)
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 17, 1001, CU)
     assert p["path"] == detfold_lib.PATH_SCALAR
     # one slot: only out and slot 0 matter
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 1, 1001, CU)
@@ -174,7 +200,22 @@ def test_plan_override(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU,
                                     dict(path=0, block=0, grid=0, unroll=0,
                                          policy=detfold_lib.POLICY_CACHED))
+    # the unhinted policy has only the direct bodies
     assert p["policy"] == detfold_lib.POLICY_CACHED and p["unroll"] == 1
+    assert p["path"] == detfold_lib.PATH_VECTOR
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU,
+                                    dict(path=detfold_lib.PATH_ROWS, block=512, grid=5, unroll=1,
+                                         policy=0))
+    assert (p["path"], p["block"], p["grid"], p["tile"]) == (detfold_lib.PATH_ROWS, 512, 5, 512)
+
+
+@pytest.mark.parametrize("W,launch", [(8, dict(block=256)), (8, dict(unroll=2)),
+                                      (8, dict(policy=2)), (1, {}), (17, {})])
+def test_plan_rejects_impossible_row_overrides(detfold_lib, W, launch):
+    cfg = dict(path=detfold_lib.PATH_ROWS, block=0, grid=0, unroll=0, policy=0)
+    cfg.update(launch)
+    with pytest.raises(detfold_lib.DetfoldError):
+        detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, 1 << 20, CU, cfg)
 
 
 @pytest.mark.parametrize("n", [1, 4, 1024, 4096, 16384, 65536])
@@ -190,8 +231,8 @@ def test_plan_decode_join_is_one_pass(detfold_lib, n):
 
 def test_plan_large_in_place_fold_streams(detfold_lib):
     p = detfold_lib.plan_fold_into(BASE, BASE + (1 << 32), 100_000_000, CU)
-    assert p["policy"] == detfold_lib.POLICY_STREAM and p["unroll"] == 1
-    assert p["block"] == 512 and p["grid"] == 25_000_000 // 512 + 1
+    assert p["policy"] == detfold_lib.POLICY_STREAM and p["path"] == detfold_lib.PATH_ROWS
+    assert p["block"] == 128 and p["tile"] == 1024 and p["grid"] == -(-25_000_000 // 1024)
 
 
 # --------------------------------------------------------------------------

@@ -235,9 +235,12 @@ def test_w16_offset_arena_shards_equal_whole(env):
     assert stacked.data_ptr() % 16 == 4
     stacked.copy_(torch.from_numpy(host))
     out_w = torch.empty(n, dtype=torch.float32, device=dev)
-    df.fold_ranks(out_w, stacked)
+    df.fold_ranks(out_w, stacked)  # the LDS row body, realigning the shifted slots
     whole = _host(out_w)
     _assert_bits(whole, want, "W=16 whole arena")
+    out_w.fill_(float("nan"))
+    df.fold_ranks_ex(out_w, stacked, path=df.PATH_SCALAR)  # the direct 4-byte body
+    _assert_bits(_host(out_w), want, "W=16 whole arena, scalar body")
     plan = df.shard_plan(n, W)
     assert [ln for _, ln in plan] == [625_002] * 3 + [625_001] * 13
     for reverse in (False, True):
@@ -264,6 +267,7 @@ def test_w16_offset_arena_shards_equal_whole(env):
 GEOMS = [dict(path=p, block=b, grid=g, unroll=u, policy=pol)
          for p in (1, 2) for b in (64, 256, 1024) for g in (0, 1, 7) for u in (1, 2, 4)
          for pol in ((0, 2) if u == 1 else (0,))]
+ROW_GEOMS = [dict(path=3, block=b, grid=g, unroll=0, policy=0) for b in (0, -1) for g in (0, 1, 7)]
 
 
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 9, 16, 17, 24])
@@ -275,7 +279,10 @@ def test_geometry_independence(env, W):
     want_s = oracle.fold_stacked_scaled(host, np.float32(1.0 / 8))
     stacked = _to_dev(torch, dev, host)
     out = torch.empty(n, dtype=torch.float32, device=dev)
-    for geom in GEOMS:
+    geoms = list(GEOMS)
+    if 2 <= W <= 16:  # the LDS row body; block -1 stands for its own size, 64*W
+        geoms += [dict(g, block=64 * W if g["block"] < 0 else 0) for g in ROW_GEOMS]
+    for geom in geoms:
         if W >= 16 and geom["unroll"] == 4 and geom["block"] == 1024:
             continue  # legal but spills registers; covered at smaller blocks
         _say("case: geometry W=%d %s" % (W, geom))
@@ -296,18 +303,22 @@ def test_alignment_phases_and_ragged_lengths(env, out_off, in_off, n, W):
     in_alloc = torch.empty(W * n + 4, dtype=torch.float32, device=dev)
     stacked = in_alloc[in_off:in_off + W * n].view(W, n)
     stacked.copy_(torch.from_numpy(host))
-    out_alloc = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev)
-    out = out_alloc[out_off:out_off + n]
-    df.fold_ranks(out, stacked)
-    full = _host(out_alloc)
-    _assert_bits(full[out_off:out_off + n], want, "W=%d n=%d offsets %d/%d" % (W, n, out_off, in_off))
-    # nothing outside [out, out + n) is written
-    assert np.isnan(full[:out_off]).all() and np.isnan(full[out_off + n:]).all()
+    paths = [df.PATH_AUTO, df.PATH_SCALAR] + ([df.PATH_ROWS] if 2 <= W <= 16 else [])
+    for path in paths:
+        out_alloc = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev)
+        out = out_alloc[out_off:out_off + n]
+        df.fold_ranks_ex(out, stacked, path=path)
+        full = _host(out_alloc)
+        _assert_bits(full[out_off:out_off + n], want,
+                     "W=%d n=%d offsets %d/%d path %d" % (W, n, out_off, in_off, path))
+        # nothing outside [out, out + n) is written
+        assert np.isnan(full[:out_off]).all() and np.isnan(full[out_off + n:]).all()
 
 
 def test_in_place_fold_alignment_phases(env):
     df, torch, dev = env
-    for n in (1, 3, 4, 5, 4095, 4096, 65537):
+    # up to 8 MiB per buffer: the latency path; above it, the streaming row body in place
+    for n in (1, 3, 4, 5, 4095, 4096, 65537, 3_000_001):
         for d_off, s_off in ((0, 0), (1, 1), (3, 3), (0, 2), (1, 0)):
             ha, hb = fold_inputs.varied(n, n, 1.0), fold_inputs.varied(n, n + 1, 1.0)
             da = torch.empty(n + 4, dtype=torch.float32, device=dev)
