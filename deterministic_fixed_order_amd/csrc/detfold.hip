@@ -47,11 +47,16 @@ constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth
 constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
 constexpr int kMaxRowsW = 16;      // widest fold the LDS row body takes (one wave per slot)
 
-// KiB of one slot each wave of the LDS row body streams per tile: about
-// 64 KiB of LDS per workgroup (two workgroups per CU), 2..16 KiB per wave.
+// KiB of one slot each wave of the LDS row body streams per tile: ceil(W/4)
+// for W >= 3, 8 for W = 2.  Measured on MI355X over W = 2..16 and 1/2/4/8 KiB
+// per wave: with every CU holding 32 waves (32/W workgroups), ceil(W/4) KiB
+// per wave keeps about 8 KiB of output tiles in flight per CU and was the
+// fastest or within 2% of it at W = 3, 4, 5, 6, 8 and 16 (W = 8: 7.1 TB/s at
+// 64 MiB per slot, against 6.4 TB/s at 8 KiB per wave).  Two-slot folds have
+// only two waves per workgroup and want long runs instead.
 constexpr int rows_kib_per_wave(int w)
 {
-    return 64 / w < 2 ? 2 : (64 / w > 16 ? 16 : 64 / w);
+    return w <= 2 ? 8 : (w + 3) / 4;
 }
 
 // Memory policy of a launch.

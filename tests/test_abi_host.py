@@ -108,16 +108,16 @@ CU = 256
 def test_plan_w8_64mib_per_slot(detfold_lib):
     n = 1 << 24
     p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 8, n, CU)
-    # LDS row body: one wave per slot, each streaming 8 KiB of its slot per tile
+    # LDS row body: one wave per slot, each streaming 2 KiB of its slot per tile
     assert p["path"] == detfold_lib.PATH_ROWS
     assert (p["head"], p["tail"], p["body"]) == (0, 0, n // 4)
-    assert p["block"] == 512 and p["tile"] == 512
-    assert p["grid"] == (n // 4) // 512 == 8192
+    assert p["block"] == 512 and p["tile"] == 128
+    assert p["grid"] == (n // 4) // 128 == 32768
     assert p["policy"] == detfold_lib.POLICY_STREAM
 
 
-@pytest.mark.parametrize("W,kib", [(2, 16), (3, 16), (4, 16), (5, 12), (7, 9), (8, 8), (9, 7),
-                                   (13, 4), (16, 4)])
+@pytest.mark.parametrize("W,kib", [(2, 8), (3, 1), (4, 1), (5, 2), (7, 2), (8, 2), (9, 3),
+                                   (12, 3), (13, 4), (16, 4)])
 def test_plan_rows_tile_per_width(detfold_lib, W, kib):
     n = 1 << 22
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, n, CU)
@@ -140,7 +140,7 @@ def test_plan_w4_gradient_arena(detfold_lib):
     n = 100_000_000
     p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 4, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS and p["body"] == n // 4 and p["tail"] == 0
-    assert p["block"] == 256 and p["tile"] == 1024 and p["grid"] == -(-(n // 4) // 1024)
+    assert p["block"] == 256 and p["tile"] == 64 and p["grid"] == -(-(n // 4) // 64)
 
 
 def test_plan_w16_offset_arena(detfold_lib):
@@ -206,7 +206,7 @@ def test_plan_override(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU,
                                     dict(path=detfold_lib.PATH_ROWS, block=512, grid=5, unroll=1,
                                          policy=0))
-    assert (p["path"], p["block"], p["grid"], p["tile"]) == (detfold_lib.PATH_ROWS, 512, 5, 512)
+    assert (p["path"], p["block"], p["grid"], p["tile"]) == (detfold_lib.PATH_ROWS, 512, 5, 128)
 
 
 @pytest.mark.parametrize("W,launch", [(8, dict(block=256)), (8, dict(unroll=2)),
@@ -232,7 +232,7 @@ def test_plan_decode_join_is_one_pass(detfold_lib, n):
 def test_plan_large_in_place_fold_streams(detfold_lib):
     p = detfold_lib.plan_fold_into(BASE, BASE + (1 << 32), 100_000_000, CU)
     assert p["policy"] == detfold_lib.POLICY_STREAM and p["path"] == detfold_lib.PATH_ROWS
-    assert p["block"] == 128 and p["tile"] == 1024 and p["grid"] == -(-25_000_000 // 1024)
+    assert p["block"] == 128 and p["tile"] == 512 and p["grid"] == -(-25_000_000 // 512)
 
 
 # --------------------------------------------------------------------------
