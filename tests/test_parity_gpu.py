@@ -442,3 +442,43 @@ def test_fold_into_next_to_a_busy_stream(env):
     _assert_bits(xa.cpu().numpy(), oracle.fold_into(ha, hb), "fold_into beside a busy stream")
     side.synchronize()
     _assert_bits(_host(big_out), oracle.fold_stacked(big.cpu().numpy()), "the busy stream's fold")
+
+
+def test_graph_replays_match_eager(env):
+    """A HIP graph holding fold_ranks, fold_ranks_scaled and fold_into must give
+    the eager results on every replay, with eager work and synchronizations
+    between the replays."""
+    df, torch, dev = env
+    W, n = 8, 300_007
+    host = fold_inputs.slots("mixed", W, n, 4242)
+    stacked = _to_dev(torch, dev, host)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    scaled = torch.empty(n, dtype=torch.float32, device=dev)
+    a0, b0 = fold_inputs.varied(n, 1, 2.0), fold_inputs.varied(n, 2, 2.0)
+    xa = _to_dev(torch, dev, a0)
+    xb = _to_dev(torch, dev, b0)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        df.fold_ranks(out, stacked)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        df.fold_ranks(out, stacked)
+        df.fold_ranks_scaled(scaled, stacked, 0.125)
+        df.fold_into(xa, xb)
+    want = oracle.fold_stacked(host)
+    want_s = oracle.fold_stacked_scaled(host, np.float32(0.125))
+    acc = a0
+    for rep in range(4):
+        out.fill_(float("nan"))
+        scaled.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        acc = oracle.fold_into(acc, b0)
+        _assert_bits(_host(out), want, "graph replay %d fold_ranks" % rep)
+        _assert_bits(_host(scaled), want_s, "graph replay %d fold_ranks_scaled" % rep)
+        _assert_bits(_host(xa), acc, "graph replay %d fold_into" % rep)
+        eager = torch.empty_like(out)
+        df.fold_ranks(eager, stacked)  # eager work between replays
+        _assert_bits(_host(eager), want, "eager between replays %d" % rep)
