@@ -49,6 +49,8 @@ WORKLOAD_NAMES = {
     "w4": "fold_ranks_scaled W=4 stacked [4][100000000] f32, mixed magnitudes, inv_w=0.25",
     "w16": "fold_ranks W=16 stacked [16][10000019] f32 at base+1 element, uniform [-1,1)",
     "join": "fold_into n=4096 f32 (16 KiB per buffer)",
+    "round": "loopback_round W=8 arenas of 16777216 f32 (64 MiB each), staged and direct",
+    "pair": "two-stream pair all-reduce at the decode-join sizes",
 }
 
 
@@ -326,6 +328,85 @@ def bench_join_only(args, torch, df, dev):
     }
 
 
+def bench_round(args, torch, df, dev):
+    """One owner-shard reduction round over W=8 arenas of 64 MiB on one device.
+
+    Bytes moved per round (direct): each owner reads its shard of all W arenas
+    and writes its own ((W+1)*n*4 over all owners), then every reduced shard is
+    read once and written to the other W-1 arenas (W*n*4).  Staged adds the
+    gather copies into the stage (2*W*n*4)."""
+    import fold_inputs
+
+    W, n = 8, 1 << 24
+    host = fold_inputs.slots("vecf", W, n, 1000)
+    arenas = [torch.from_numpy(host[r]).to(dev) for r in range(W)]
+    stage = torch.empty(df.round_stage_elems(n, W), dtype=torch.float32, device=dev)
+    timer = Timer(torch, torch.cuda.current_stream(dev))
+    res = {}
+    for mode in ("direct", "staged"):
+        direct = mode == "direct"
+
+        def step():
+            df.loopback_round(arenas, None if direct else stage, direct=direct)
+        for _ in range(args.warmup):
+            step()
+        ms = timer.region(step, args.steps) / args.steps
+        moved = (2 * W + 1) * n * 4 if direct else (4 * W + 1) * n * 4
+        res[mode] = {"ms_per_round": round(ms, 4), "bytes_moved": moved,
+                     "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+        log("round %s: %.3f ms per round, %.1f GB/s of bytes moved" % (mode, ms, res[mode]["GBps"]))
+    d = res["direct"]
+    return {
+        "metric": "one-GPU fixed-order reduction round, W=8 arenas of 64 MiB (bytes moved / time)",
+        "value": d["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": d["ms_per_round"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES["round"], "W": W, "len": n}, "round": res,
+    }
+
+
+def bench_pair(args, torch, df, dev):
+    """Two ranks on two streams: one all-reduce per call (push, event, fold on
+    both ranks), back-to-back, and one call with a host synchronization."""
+    import fold_inputs
+
+    link = df.PairLink(max(JOIN_SIZES), device=dev)
+    rows = []
+    for n in JOIN_SIZES:
+        xa = torch.from_numpy(fold_inputs.vecf(n, 11 + n)).to(dev)
+        xb = torch.from_numpy(fold_inputs.vecf(n, 77 + n)).to(dev)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            link.all_reduce(xa, xb)
+        torch.cuda.synchronize()
+        reps = 500
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            link.all_reduce(xa, xb)
+        torch.cuda.synchronize()
+        b2b = (time.perf_counter() - t0) / reps * 1e6
+        one = []
+        for _ in range(200):
+            t1 = time.perf_counter()
+            link.all_reduce(xa, xb)
+            for st in link.streams:
+                st.synchronize()
+            one.append((time.perf_counter() - t1) * 1e6)
+        rows.append({"n": n, "back_to_back_us_per_call": round(b2b, 3),
+                     "enqueue_to_complete_us_median": round(statistics.median(one), 3)})
+        log("pair all-reduce n=%6d: %.2f us/call back-to-back, %.2f us call+sync"
+            % (n, b2b, statistics.median(one)))
+    at16 = next(r for r in rows if r["n"] == 4096)
+    return {
+        "metric": "two-stream pair all-reduce at 16 KiB (enqueue to completion)",
+        "value": at16["enqueue_to_complete_us_median"], "unit": "us/call", "n_gpus": 1,
+        "steps": 500, "warmup": 20, "ms_per_step": at16["enqueue_to_complete_us_median"] / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": WORKLOAD_NAMES["pair"], "n": 4096},
+        "pair": rows,
+    }
+
+
 def sweep(args, torch, df, dev):
     """Launch-geometry sweep of the headline fold (all results bit-checked
     against the default launch's output)."""
@@ -384,7 +465,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join"], default="w8")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join", "round", "pair"], default="w8")
     ap.add_argument("--singles", type=int, default=30, help="scrubbed single-launch samples")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -412,6 +493,10 @@ def main(argv=None) -> int:
         res = sweep(args, torch, df, dev)
     elif args.workload == "join":
         res = bench_join_only(args, torch, df, dev)
+    elif args.workload == "round":
+        res = bench_round(args, torch, df, dev)
+    elif args.workload == "pair":
+        res = bench_pair(args, torch, df, dev)
     else:
         res = bench_fold(args, torch, df, dev)
     res["kernel_source_sha256_16"] = kernel_source_hash()

@@ -12,6 +12,9 @@ PyTorch is used for device memory and streams only.
     fold_ranks(out, stacked)                 out = s_0 + s_1 + ... + s_{W-1}, ascending
     fold_ranks_scaled(out, stacked, inv_w)   the same, then * inv_w
     fold_into(dst, stage)                    dst = dst + stage (in place)
+    fold_slots(out, [s_0, ..., s_{W-1}])     the fold over separate buffers (W <= 16)
+    loopback_round(arenas, stage=None, ...)  one owner-shard reduction round over W arenas
+    PairLink(...).all_reduce(x0, x1)         two-stream (two-rank) all-reduce on one device
 
 ``stacked`` is a ``[W, len]`` float32 CUDA/HIP tensor (row r = slot r); a view
 with a storage offset is fine as long as it is contiguous.
@@ -28,12 +31,14 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
+ROUND_REVERSE_DELIVERY, ROUND_DIRECT = 1, 2
 
 EXPORTS = (
     "fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror", "detfold_abi_version",
     "detfold_shard_plan", "detfold_plan_fold_ranks", "detfold_plan_fold_into",
-    "detfold_fold_ranks_ex",
+    "detfold_fold_ranks_ex", "fold_slots", "fold_slots_scaled", "detfold_loopback_round",
+    "detfold_pair_link_init", "detfold_pair_all_reduce",
 )
 
 
@@ -46,6 +51,12 @@ class DetfoldError(RuntimeError):
 class Launch(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32), ("policy", ctypes.c_int32)]
+
+
+class PairLinkC(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p * 2), ("stage", ctypes.c_void_p * 2),
+                ("capacity", ctypes.c_int64), ("pushed", ctypes.c_void_p * 2),
+                ("folded", ctypes.c_void_p * 2)]
 
 
 class Plan(ctypes.Structure):
@@ -85,9 +96,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(Launch), ctypes.POINTER(Plan)]
     lib.detfold_plan_fold_into.argtypes = [ctypes.c_size_t, ctypes.c_size_t, i64, i32,
                                            ctypes.POINTER(Plan)]
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.fold_slots.argtypes = [f32p, pp, i32, i64, vp]
+    lib.fold_slots_scaled.argtypes = [f32p, pp, i32, i64, ctypes.c_float, vp]
+    lib.detfold_loopback_round.argtypes = [pp, i32, i64, f32p, i64, i32, vp]
+    lib.detfold_pair_link_init.argtypes = [ctypes.POINTER(PairLinkC)]
+    lib.detfold_pair_all_reduce.argtypes = [ctypes.POINTER(PairLinkC), f32p, f32p, i64]
     for name in ("fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_fold_ranks_ex",
                  "detfold_abi_version", "detfold_shard_plan", "detfold_plan_fold_ranks",
-                 "detfold_plan_fold_into"):
+                 "detfold_plan_fold_into", "fold_slots", "fold_slots_scaled",
+                 "detfold_loopback_round", "detfold_pair_link_init", "detfold_pair_all_reduce"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.detfold_abi_version() != ABI_VERSION:
         raise RuntimeError("libdetfold ABI mismatch")
@@ -171,6 +189,103 @@ def fold_ranks_ex(out, stacked, *, scaled: bool = False, inv_w: float = 1.0, pat
     _check(load().detfold_fold_ranks_ex(out.data_ptr(), stacked.data_ptr(), W, n, int(scaled),
                                         float(inv_w), ctypes.byref(cfg),
                                         _stream_handle(out, stream)), "detfold_fold_ranks_ex")
+
+
+def _ptr_array(tensors):
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _same_len_slots(out, slots):
+    _f32_device(out, "out")
+    if not slots:
+        raise ValueError("need at least one slot")
+    for i, t in enumerate(slots):
+        _f32_device(t, "slots[%d]" % i)
+        if t.numel() != out.numel():
+            raise ValueError("slot %d has %d elements, out %d" % (i, t.numel(), out.numel()))
+        if t.device != out.device:
+            raise ValueError("slot %d is on another device" % i)
+
+
+def fold_slots(out, slots, stream=None) -> None:
+    """``out = ((slots[0] + slots[1]) + ...) + slots[W-1]`` over separate tensors
+    (W <= 16); ``out`` may be one of the slots (in place)."""
+    _same_len_slots(out, slots)
+    _check(load().fold_slots(out.data_ptr(), _ptr_array(slots), len(slots), out.numel(),
+                             _stream_handle(out, stream)), "fold_slots")
+
+
+def fold_slots_scaled(out, slots, inv_w: float, stream=None) -> None:
+    """``fold_slots`` followed by one binary32 multiply by ``inv_w``."""
+    _same_len_slots(out, slots)
+    _check(load().fold_slots_scaled(out.data_ptr(), _ptr_array(slots), len(slots), out.numel(),
+                                    float(inv_w), _stream_handle(out, stream)), "fold_slots_scaled")
+
+
+def round_stage_elems(n: int, world: int) -> int:
+    """Floats of staging a staged ``loopback_round`` needs: W * ceil(n / W)."""
+    return world * (-(-n // world)) if world > 0 else 0
+
+
+def loopback_round(arenas, stage=None, *, reverse_delivery: bool = False, direct: bool = False,
+                   stream=None) -> None:
+    """One fixed-order reduction round across the W arenas (one device).
+
+    Afterwards every arena holds the ascending-rank fold of all the arenas'
+    previous contents.  Staged (default) gathers each owner's shard copies into
+    ``stage`` (at least ``round_stage_elems(n, W)`` floats) before folding;
+    ``direct`` folds straight from the arenas."""
+    if not arenas:
+        raise ValueError("need at least one arena")
+    n = arenas[0].numel()
+    for i, a in enumerate(arenas):
+        _f32_device(a, "arenas[%d]" % i)
+        if a.numel() != n:
+            raise ValueError("arena %d has %d elements, arena 0 has %d" % (i, a.numel(), n))
+    flags = (ROUND_REVERSE_DELIVERY if reverse_delivery else 0) | (ROUND_DIRECT if direct else 0)
+    stage_ptr, stage_elems = None, 0
+    if stage is not None:
+        _f32_device(stage, "stage")
+        stage_ptr, stage_elems = stage.data_ptr(), stage.numel()
+    _check(load().detfold_loopback_round(_ptr_array(arenas), len(arenas), n, stage_ptr, stage_elems,
+                                         flags, _stream_handle(arenas[0], stream)),
+           "loopback_round")
+
+
+class PairLink:
+    """Two ranks on one device, each a stream, joined by staging buffers and
+    events (the library's ``detfold_pair_link``).  ``all_reduce(x0, x1)`` leaves
+    ``x0 + x1`` in both, folded on each rank's own stream."""
+
+    def __init__(self, capacity: int, device=None, streams=None):
+        import torch
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.streams = list(streams) if streams is not None else [torch.cuda.Stream(device=dev) for _ in range(2)]
+        self.stage = [torch.empty(max(capacity, 1), dtype=torch.float32, device=dev) for _ in range(2)]
+        # timing disabled: the events only order the two streams
+        self.pushed = [torch.cuda.Event(enable_timing=False) for _ in range(2)]
+        self.folded = [torch.cuda.Event(enable_timing=False) for _ in range(2)]
+        for e in self.pushed + self.folded:
+            e.record(self.streams[0])  # materialise the underlying event
+        torch.cuda.synchronize(dev)
+        self.capacity = capacity
+        self._c = PairLinkC()
+        for r in range(2):
+            self._c.stream[r] = self.streams[r].cuda_stream
+            self._c.stage[r] = self.stage[r].data_ptr()
+            self._c.pushed[r] = self.pushed[r].cuda_event  # the raw hipEvent_t
+            self._c.folded[r] = self.folded[r].cuda_event
+        self._c.capacity = capacity
+        _check(load().detfold_pair_link_init(ctypes.byref(self._c)), "pair_link_init")
+
+    def all_reduce(self, x0, x1) -> None:
+        _f32_device(x0, "x0")
+        _f32_device(x1, "x1")
+        if x0.numel() != x1.numel():
+            raise ValueError("x0 has %d elements, x1 %d" % (x0.numel(), x1.numel()))
+        _check(load().detfold_pair_all_reduce(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
+                                              x0.numel()), "pair_all_reduce")
 
 
 def shard_plan(n: int, world: int) -> list[tuple[int, int]]:

@@ -30,6 +30,7 @@
 //    disabled, and f32 denormals enabled (the HIP default on gfx9), so every
 //    add is a single v_add_f32 under IEEE round-to-nearest-even.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -273,10 +274,29 @@ template <int W> struct RowsShape {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Slot base pointers of the LDS row body, passed by value in the kernel
+// arguments (slot r of a stacked arena is stacked + r*len; fold_slots takes
+// them from the caller).
+struct SlotTable {
+    const float *p[kMaxRowsW];
+};
+
+template <int W, bool SCALED>
+__device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slots, int64_t i,
+                                               float inv_w)
+{
+    float acc = slots.p[0][i];
+#pragma unroll
+    for (int r = 1; r < W; ++r)
+        acc = acc + slots.p[r][i];
+    if constexpr (SCALED)
+        acc = acc * inv_w;
+    out[i] = acc;
+}
+
 template <int W, bool ALIGNED, bool SCALED>
-__global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, const float *s0, const float *s1,
-                                                      int64_t stride, int64_t len, int64_t head,
-                                                      float inv_w)
+__global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
+                                                      int64_t head, float inv_w)
 {
     constexpr int LPW = RowsShape<W>::LPW, T = RowsShape<W>::T;
     constexpr int LOADS = ALIGNED ? LPW : LPW + 1;  // one more block when the slot is shifted
@@ -287,10 +307,11 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, const float *s
     const int64_t tail0 = head + (groups << 2);
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid < head + (len - tail0))
-        fold_one<W, SCALED>(out, s0, s1, stride, W, gid < head ? gid : tail0 + (gid - head), inv_w);
+        fold_one_table<W, SCALED>(out, slots, gid < head ? gid : tail0 + (gid - head), inv_w);
 
-    const uint32_t lane = threadIdx.x & 63, r = threadIdx.x >> 6;
-    const float *slot = r == 0 ? s0 : s1 + (int64_t)(r - 1) * stride;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's slot
+    const float *slot = slots.p[r];
     for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
@@ -317,8 +338,7 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, const float *s
             } else {
 #pragma unroll
                 for (int q = 0; q < W; ++q) {
-                    const float *sq = q == 0 ? s0 : s1 + (int64_t)(q - 1) * stride;
-                    const uint32_t d = (uint32_t)(((uintptr_t)(sq + e0) >> 2) & 3);
+                    const uint32_t d = (uint32_t)(((uintptr_t)(slots.p[q] + e0) >> 2) & 3);
                     const float *row = reinterpret_cast<const float *>(&rows[q][0]) + d + 4 * t;
                     const f4 v = {row[0], row[1], row[2], row[3]};
                     acc = q == 0 ? v : acc + v;
@@ -332,6 +352,50 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, const float *s
     }
 }
 
+// Byte movement for the one-device rounds: copy `n` floats from `src` into
+// every one of `ndst` destinations (src read once).  VEC: src and every
+// destination share one 16-byte phase -- 16-byte groups after `head` scalar
+// elements, `tail` after them; otherwise one 4-byte element per thread.  No
+// arithmetic touches the data.
+template <bool VEC, int POL>
+__global__ __launch_bounds__(kMaxBlock) void k_copy_out(SlotTable dsts, int ndst, const float *src,
+                                                        int64_t n, int64_t head)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    if constexpr (VEC) {
+        const int64_t groups = (n - head) >> 2;
+        const int64_t tail0 = head + (groups << 2);
+        if (gid < head + (n - tail0)) {
+            const int64_t i = gid < head ? gid : tail0 + (gid - head);
+            const float v = src[i];
+            for (int d = 0; d < ndst; ++d)
+                const_cast<float *>(dsts.p[d])[i] = v;
+        }
+        const f4 *s4 = reinterpret_cast<const f4 *>(src + head);
+        for (int64_t g = gid; g < groups; g += nthreads) {
+            f4 v;
+            if constexpr (POL == kStream)
+                v = __builtin_nontemporal_load(s4 + g);
+            else
+                v = s4[g];
+            for (int d = 0; d < ndst; ++d) {
+                f4 *d4 = reinterpret_cast<f4 *>(const_cast<float *>(dsts.p[d]) + head) + g;
+                if constexpr (POL == kStream)
+                    __builtin_nontemporal_store(v, d4);
+                else
+                    *d4 = v;
+            }
+        }
+    } else {
+        for (int64_t i = gid; i < n; i += nthreads) {
+            const float v = src[i];
+            for (int d = 0; d < ndst; ++d)
+                const_cast<float *>(dsts.p[d])[i] = v;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: planning (pure integer logic, no HIP calls)
 
@@ -340,6 +404,17 @@ struct Geometry {
     int64_t stride;         // elements between slots r and r+1 for r >= 1
     int32_t w;
     int64_t len;
+    // Every slot's base address when the slots are not one stacked arena
+    // (fold_slots); otherwise empty and derived from s0, s1 and stride.
+    bool has_table = false;
+    uintptr_t table[kMaxRowsW] = {};
+
+    uintptr_t slot(int32_t r) const
+    {
+        if (has_table)
+            return table[r];
+        return r == 0 ? s0 : s1 + (uintptr_t)((r - 1) * stride) * 4;
+    }
 };
 
 inline int phase16(uintptr_t a) { return (int)((a >> 2) & 3); }
@@ -348,6 +423,12 @@ inline int phase16(uintptr_t a) { return (int)((a >> 2) & 3); }
 bool vector_legal(const Geometry &g)
 {
     const int p = phase16(g.out);
+    if (g.has_table) {
+        for (int32_t r = 0; r < g.w; ++r)
+            if (phase16(g.table[r]) != p)
+                return false;
+        return true;
+    }
     if (phase16(g.s0) != p)
         return false;
     if (g.w >= 2 && phase16(g.s1) != p)
@@ -405,6 +486,9 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
 
     const bool vec_ok = vector_legal(g);
     const bool rows_ok = g.w >= 2 && g.w <= kMaxRowsW;
+    if (g.has_table && g.w >= 2 && (o.path == DETFOLD_PATH_VECTOR || o.path == DETFOLD_PATH_SCALAR ||
+                                    policy == DETFOLD_POLICY_CACHED))
+        return DETFOLD_EINVAL;  // separate slot buffers have only the LDS row body
     int path = o.path;
     if (path == DETFOLD_PATH_AUTO) {
         if (rows_ok && policy == DETFOLD_POLICY_STREAM)
@@ -573,8 +657,7 @@ scalar_kernel_t pick_scalar_w(int unroll, int policy)
     }
 }
 
-typedef void (*rows_kernel_t)(float *, const float *, const float *, int64_t, int64_t, int64_t,
-                              float);
+typedef void (*rows_kernel_t)(float *, SlotTable, int64_t, int64_t, float);
 
 template <int W, bool SCALED>
 rows_kernel_t pick_rows_w(bool aligned)
@@ -630,8 +713,18 @@ scalar_kernel_t pick_scalar(int32_t w, int unroll, int policy)
     }
 }
 
+// Launch a kernel; with `done`, the event is recorded by the dispatch itself
+// when the kernel completes (cheaper than a separate event record).
+hipError_t launch(const void *k, dim3 grid, dim3 block, void **args, hipStream_t stream,
+                  hipEvent_t done)
+{
+    if (done)
+        return hipExtLaunchKernel(k, grid, block, args, 0, stream, nullptr, done, 0);
+    return hipLaunchKernel(k, grid, block, args, 0, stream);
+}
+
 int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv_w,
-                hipStream_t stream)
+                hipStream_t stream, hipEvent_t done = nullptr)
 {
     float *out = reinterpret_cast<float *>(g.out);
     const float *s0 = reinterpret_cast<const float *>(g.s0);
@@ -645,18 +738,21 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
     hipError_t e;
     if (p.path == DETFOLD_PATH_ROWS) {
         rows_kernel_t k = scaled ? pick_rows<true>(w, vector_legal(g)) : pick_rows<false>(w, vector_legal(g));
-        void *args[] = {&out, &s0, &s1, &stride, &len, &head, &inv_w};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
+        SlotTable slots = {};
+        for (int32_t r = 0; r < w; ++r)
+            slots.p[r] = reinterpret_cast<const float *>(g.slot(r));
+        void *args[] = {&out, &slots, &len, &head, &inv_w};
+        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
     } else if (p.path == DETFOLD_PATH_VECTOR) {
         vector_kernel_t k = scaled ? pick_vector<true>(w, p.unroll, policy)
                                    : pick_vector<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
+        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
     } else {
         scalar_kernel_t k = scaled ? pick_scalar<true>(w, p.unroll, policy)
                                    : pick_scalar<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &inv_w};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
+        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
     }
     return e == hipSuccess ? DETFOLD_OK : DETFOLD_ELAUNCH;
 }
@@ -694,6 +790,259 @@ int plan_into(const Geometry &g, int32_t cu_count, detfold_plan *p)
         return make_plan(g, cu_count, &o, DETFOLD_POLICY_CACHED, p);
     }
     return make_plan(g, cu_count, nullptr, DETFOLD_POLICY_STREAM, p);
+}
+
+// ---------------------------------------------------------------------------
+// Separate slot buffers (fold_slots) and the one-GPU rounds built on them
+
+// out may be exactly one (or more) of the slots -- the fold then runs in place,
+// every element read before it is written by the same workgroup -- but may not
+// partly overlap any slot.
+int check_slots_args(const float *out, const float *const *slots, int32_t W, int64_t len)
+{
+    if (W < 1 || W > kMaxRowsW || len < 0)
+        return DETFOLD_EINVAL;
+    if (len == 0)
+        return DETFOLD_OK;
+    if (!out || !slots || (((uintptr_t)out) & 3) || len > INT64_MAX / 4)
+        return DETFOLD_EINVAL;
+    for (int32_t r = 0; r < W; ++r) {
+        if (!slots[r] || (((uintptr_t)slots[r]) & 3))
+            return DETFOLD_EINVAL;
+        if (slots[r] != out &&
+            ranges_overlap((uintptr_t)out, (uint64_t)len * 4, (uintptr_t)slots[r], (uint64_t)len * 4))
+            return DETFOLD_EOVERLAP;
+    }
+    return DETFOLD_OK;
+}
+
+Geometry slots_geometry(const float *out, const float *const *slots, int32_t W, int64_t len)
+{
+    Geometry g{(uintptr_t)out, (uintptr_t)slots[0], W >= 2 ? (uintptr_t)slots[1] : (uintptr_t)slots[0],
+               0, W, len};
+    g.has_table = true;
+    for (int32_t r = 0; r < W; ++r)
+        g.table[r] = (uintptr_t)slots[r];
+    return g;
+}
+
+// Launch the fold of separate slots (arguments already checked, len > 0).
+int launch_slots(const float *out, const float *const *slots, int32_t W, int64_t len, bool scaled,
+                 float inv_w, int32_t cu, hipStream_t stream)
+{
+    const Geometry g = slots_geometry(out, slots, W, len);
+    detfold_plan p;
+    int rc = make_plan(g, cu, nullptr, DETFOLD_POLICY_STREAM, &p);
+    if (rc != DETFOLD_OK)
+        return rc;
+    return launch_plan(g, p, scaled, inv_w, stream);
+}
+
+int run_slots(float *out, const float *const *slots, int32_t W, int64_t len, bool scaled,
+              float inv_w, void *stream)
+{
+    int rc = check_slots_args(out, slots, W, len);
+    if (rc != DETFOLD_OK || len == 0)
+        return rc;
+    int32_t cu = 0;
+    if ((rc = current_cu_count(&cu)) != DETFOLD_OK)
+        return rc;
+    return launch_slots(out, slots, W, len, scaled, inv_w, cu, static_cast<hipStream_t>(stream));
+}
+
+// Copy len floats from src to each of ndst destinations with k_copy_out.
+// Payloads up to kLatencyBytes take no cache hints (they are read again
+// soon); larger ones stream.  One pass of 256-thread workgroups, capped at 8
+// per CU with the rest covered by the grid-stride loop.
+int copy_out(float *const *dsts, int ndst, const float *src, int64_t len, int32_t cu,
+             hipStream_t stream, hipEvent_t done = nullptr)
+{
+    if (len == 0 || ndst == 0)
+        return DETFOLD_OK;
+    SlotTable t = {};
+    bool vec = true;
+    const int ph = phase16((uintptr_t)src);
+    for (int d = 0; d < ndst; ++d) {
+        t.p[d] = dsts[d];
+        vec = vec && phase16((uintptr_t)dsts[d]) == ph;
+    }
+    int64_t head = (4 - ph) & 3;
+    if (head > len)
+        head = len;
+    const int64_t units = vec ? ((len - head) >> 2) + 6 : len;
+    const int block = 256;
+    int64_t grid = (units + block - 1) / block;
+    const int64_t cap = (int64_t)cu * 8;
+    if (grid > cap)
+        grid = cap;
+    if (grid < 1)
+        grid = 1;
+    const bool stream_pol = len * 4 > kLatencyBytes;
+    const void *k = vec ? (stream_pol ? (const void *)k_copy_out<true, kStream> : (const void *)k_copy_out<true, kCached>)
+                        : (stream_pol ? (const void *)k_copy_out<false, kStream> : (const void *)k_copy_out<false, kCached>);
+    void *args[] = {&t, &ndst, &src, &len, &head};
+    return launch(k, dim3((unsigned)grid), dim3(block), args, stream, done) == hipSuccess ? DETFOLD_OK
+                                                                                        : DETFOLD_ELAUNCH;
+}
+
+int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length)
+{
+    if (world < 1 || n < 0 || !start || !length)
+        return DETFOLD_EINVAL;
+    const int64_t q = n / world, r = n % world;
+    int64_t s = 0;
+    for (int32_t p = 0; p < world; ++p) {
+        const int64_t l = q + (p < r ? 1 : 0);
+        start[p] = s;
+        length[p] = l;
+        s += l;
+    }
+    return DETFOLD_OK;
+}
+
+int check_round_args(float *const *arenas, int32_t W, int64_t n, const float *stage,
+                     int64_t stage_elems, int32_t flags)
+{
+    if (W < 1 || W > kMaxRowsW || n < 0 || (flags & ~(DETFOLD_ROUND_REVERSE_DELIVERY | DETFOLD_ROUND_DIRECT)))
+        return DETFOLD_EINVAL;
+    if (W == 1 || n == 0)
+        return DETFOLD_OK;
+    if (!arenas || n > INT64_MAX / 4 / W)
+        return DETFOLD_EINVAL;
+    for (int32_t r = 0; r < W; ++r) {
+        if (!arenas[r] || (((uintptr_t)arenas[r]) & 3))
+            return DETFOLD_EINVAL;
+        for (int32_t q = 0; q < r; ++q)
+            if (ranges_overlap((uintptr_t)arenas[r], (uint64_t)n * 4, (uintptr_t)arenas[q], (uint64_t)n * 4))
+                return DETFOLD_EOVERLAP;
+    }
+    if (!(flags & DETFOLD_ROUND_DIRECT)) {
+        const int64_t need = (int64_t)W * ((n + W - 1) / W);
+        if (!stage || (((uintptr_t)stage) & 3) || stage_elems < need)
+            return DETFOLD_EINVAL;
+        for (int32_t r = 0; r < W; ++r)
+            if (ranges_overlap((uintptr_t)stage, (uint64_t)need * 4, (uintptr_t)arenas[r], (uint64_t)n * 4))
+                return DETFOLD_EOVERLAP;
+    }
+    return DETFOLD_OK;
+}
+
+// One fixed-order reduction round over W arenas on one device (mamba-rs
+// src/dist/reducer.rs, LoopbackWorld::run_round, with the transport's
+// owner-shard dataflow of reduce_sum_fixed_order_nccl):
+//   A. every owner p gathers the W copies of its shard, slot = source rank,
+//      and folds them in ascending slot order into its own arena's shard;
+//   B. every owner's reduced shard is copied to the other W-1 arenas.
+// Staged (the transport's shape): the gather copies each source's shard into
+// `stage` ([W][l_p], slot = source rank) in ascending or, with
+// DETFOLD_ROUND_REVERSE_DELIVERY, descending source order, then fold_ranks
+// folds `stage`.  Direct: the owner folds straight from the W arenas
+// (fold_slots, in place on its own shard), since on one device every arena is
+// already in the same HBM.  Bytes move by device-to-device copies only, so the
+// bits are the fold's whatever the mode or the delivery order.
+int run_round(float *const *arenas, int32_t W, int64_t n, float *stage, int32_t flags,
+              hipStream_t stream)
+{
+    int32_t cu = 0;
+    int rc = current_cu_count(&cu);
+    if (rc != DETFOLD_OK)
+        return rc;
+    int64_t start[kMaxRowsW], length[kMaxRowsW];
+    balanced_shards(n, W, start, length);
+    const bool direct = flags & DETFOLD_ROUND_DIRECT;
+    const bool reverse = flags & DETFOLD_ROUND_REVERSE_DELIVERY;
+    for (int32_t me = 0; me < W; ++me) {
+        const int64_t s = start[me], l = length[me];
+        if (l == 0)
+            continue;
+        if (direct) {
+            const float *slots[kMaxRowsW];
+            for (int32_t r = 0; r < W; ++r)
+                slots[r] = arenas[r] + s;
+            rc = launch_slots(arenas[me] + s, slots, W, l, false, 1.0f, cu, stream);
+        } else {
+            for (int32_t k = 0; k < W && rc == DETFOLD_OK; ++k) {
+                const int32_t src = reverse ? W - 1 - k : k;
+                float *slot = stage + (int64_t)src * l;
+                rc = copy_out(&slot, 1, arenas[src] + s, l, cu, stream);
+            }
+            if (rc == DETFOLD_OK) {
+                const Geometry g = ranks_geometry((uintptr_t)(arenas[me] + s), (uintptr_t)stage, W, l);
+                detfold_plan p;
+                rc = make_plan(g, cu, nullptr, DETFOLD_POLICY_STREAM, &p);
+                if (rc == DETFOLD_OK)
+                    rc = launch_plan(g, p, false, 1.0f, stream);
+            }
+        }
+        if (rc != DETFOLD_OK)
+            return rc;
+    }
+    for (int32_t o = 0; o < W; ++o) {  // owner o's shard, read once, written to the other arenas
+        float *dsts[kMaxRowsW];
+        int nd = 0;
+        for (int32_t r = 0; r < W; ++r)
+            if (r != o)
+                dsts[nd++] = arenas[r] + start[o];
+        if ((rc = copy_out(dsts, nd, arenas[o] + start[o], length[o], cu, stream)) != DETFOLD_OK)
+            return rc;
+    }
+    return DETFOLD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Two ranks on one device (memra-engine tests/tp_ar_gpu.rs, ArLink's pipeline
+// arm, on the same-device emulation its module note describes): each rank is
+// a stream; a rank pushes its partial into the peer's staging buffer (a device
+// copy), and once the peer's push has landed in its own staging buffer it
+// folds in place.  Ordering is by events on the streams only -- no device
+// flag, no spin -- so neither rank's kernel ever waits on the other's.
+
+int check_pair_args(const detfold_pair_link *k, const float *x0, const float *x1, int64_t n)
+{
+    if (!k || n < 0 || n > k->capacity || !k->pushed[0] || !k->pushed[1] || !k->folded[0] ||
+        !k->folded[1])
+        return DETFOLD_EINVAL;
+    if (n == 0)
+        return DETFOLD_OK;
+    const float *p[4] = {x0, x1, k->stage[0], k->stage[1]};
+    for (int i = 0; i < 4; ++i) {
+        if (!p[i] || (((uintptr_t)p[i]) & 3) || n > INT64_MAX / 4)
+            return DETFOLD_EINVAL;
+        for (int j = 0; j < i; ++j)
+            if (ranges_overlap((uintptr_t)p[i], (uint64_t)n * 4, (uintptr_t)p[j], (uint64_t)n * 4))
+                return DETFOLD_EOVERLAP;
+    }
+    return DETFOLD_OK;
+}
+
+int run_pair(const detfold_pair_link *k, float *x0, float *x1, int64_t n)
+{
+    int32_t cu = 0;
+    int rc = current_cu_count(&cu);
+    if (rc != DETFOLD_OK)
+        return rc;
+    float *x[2] = {x0, x1};
+    hipStream_t st[2] = {static_cast<hipStream_t>(k->stream[0]), static_cast<hipStream_t>(k->stream[1])};
+    for (int r = 0; r < 2; ++r) {
+        const int peer = 1 - r;
+        // the peer's previous fold has finished reading the staging buffer we refill
+        if (hipStreamWaitEvent(st[r], static_cast<hipEvent_t>(k->folded[peer]), 0) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+        float *dst = k->stage[peer];
+        if ((rc = copy_out(&dst, 1, x[r], n, cu, st[r], static_cast<hipEvent_t>(k->pushed[r]))) != DETFOLD_OK)
+            return rc;
+    }
+    for (int r = 0; r < 2; ++r) {
+        const int peer = 1 - r;
+        if (hipStreamWaitEvent(st[r], static_cast<hipEvent_t>(k->pushed[peer]), 0) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+        const Geometry g = into_geometry((uintptr_t)x[r], (uintptr_t)k->stage[r], n);
+        detfold_plan p;
+        if ((rc = plan_into(g, cu, &p)) != DETFOLD_OK ||
+            (rc = launch_plan(g, p, false, 1.0f, st[r], static_cast<hipEvent_t>(k->folded[r]))) != DETFOLD_OK)
+            return rc;
+    }
+    return DETFOLD_OK;
 }
 
 }  // namespace
@@ -752,17 +1101,7 @@ int detfold_abi_version(void) { return DETFOLD_ABI_VERSION; }
 
 int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length)
 {
-    if (world < 1 || n < 0 || !start || !length)
-        return DETFOLD_EINVAL;
-    const int64_t q = n / world, r = n % world;
-    int64_t s = 0;
-    for (int32_t p = 0; p < world; ++p) {
-        const int64_t l = q + (p < r ? 1 : 0);
-        start[p] = s;
-        length[p] = l;
-        s += l;
-    }
-    return DETFOLD_OK;
+    return balanced_shards(n, world, start, length);
 }
 
 int detfold_plan_fold_ranks(uintptr_t out, uintptr_t stacked, int32_t W, int64_t len,
@@ -788,6 +1127,44 @@ int detfold_plan_fold_into(uintptr_t dst, uintptr_t stage, int64_t n, int32_t cu
     if (rc != DETFOLD_OK)
         return rc;
     return plan_into(into_geometry(dst, stage, n), cu_count, plan);
+}
+
+int fold_slots(float *out, const float *const *slots, int32_t W, int64_t len, void *stream)
+{
+    return run_slots(out, slots, W, len, false, 1.0f, stream);
+}
+
+int fold_slots_scaled(float *out, const float *const *slots, int32_t W, int64_t len, float inv_w,
+                      void *stream)
+{
+    return run_slots(out, slots, W, len, true, inv_w, stream);
+}
+
+int detfold_loopback_round(float *const *arenas, int32_t W, int64_t n, float *stage,
+                           int64_t stage_elems, int32_t flags, void *stream)
+{
+    int rc = check_round_args(arenas, W, n, stage, stage_elems, flags);
+    if (rc != DETFOLD_OK || W == 1 || n == 0)
+        return rc;
+    return run_round(arenas, W, n, stage, flags, static_cast<hipStream_t>(stream));
+}
+
+int detfold_pair_link_init(const detfold_pair_link *link)
+{
+    if (!link || !link->folded[0] || !link->folded[1] || !link->pushed[0] || !link->pushed[1])
+        return DETFOLD_EINVAL;
+    for (int r = 0; r < 2; ++r)
+        if (hipEventRecord(static_cast<hipEvent_t>(link->folded[r]), static_cast<hipStream_t>(link->stream[r])) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+    return DETFOLD_OK;
+}
+
+int detfold_pair_all_reduce(const detfold_pair_link *link, float *x0, float *x1, int64_t n)
+{
+    int rc = check_pair_args(link, x0, x1, n);
+    if (rc != DETFOLD_OK || n == 0)
+        return rc;
+    return run_pair(link, x0, x1, n);
 }
 
 }  // extern "C"

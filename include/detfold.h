@@ -98,11 +98,102 @@ int fold_into(float *dst, const float *stage, int64_t n, void *stream);
 int fold_ranks_scaled(float *out, const float *stacked, int32_t W, int64_t len, float inv_w,
                       void *stream);
 
+/*
+ * fold_slots -- out[i] = ((s_0[i] + s_1[i]) + ...) + s_{W-1}[i] over W separate buffers
+ *
+ * The same fold as fold_ranks when the addends do not sit in one stacked arena
+ * (for example W per-rank arenas on one device, as in mamba-rs
+ * src/dist/reducer.rs LoopbackWorld, or buffers of another device mapped into
+ * this one's address space).
+ *   out      device pointer, written (len floats).  It may be identical to one
+ *            or more of the slots (the fold then runs in place); any other
+ *            overlap with a slot is DETFOLD_EOVERLAP.
+ *   slots    HOST array of W device pointers, each to len floats (read); the
+ *            pointers are passed to the kernel by value, the array may be
+ *            reused as soon as the call returns.  Slots may overlap each other.
+ *   W        1 <= W <= 16
+ *   len      elements, >= 0
+ * Errors: DETFOLD_EINVAL (also for W > 16), DETFOLD_EOVERLAP, DETFOLD_EDEVICE,
+ * DETFOLD_ELAUNCH.
+ */
+int fold_slots(float *out, const float *const *slots, int32_t W, int64_t len, void *stream);
+
+/* fold_slots followed by one binary32 multiply of each sum by inv_w. */
+int fold_slots_scaled(float *out, const float *const *slots, int32_t W, int64_t len, float inv_w,
+                      void *stream);
+
+/*
+ * detfold_loopback_round -- one fixed-order reduction round across W arenas on
+ * one device: afterwards every arena holds, bit for bit, the ascending-rank
+ * fold of the W arenas' original contents.
+ *
+ * The dataflow of mamba-rs src/dist/reducer.rs (LoopbackWorld::run_round and
+ * the owner-shard exchange of reduce_sum_fixed_order_nccl): [0, n) is split
+ * into W contiguous owner shards (detfold_shard_plan); owner p folds the W
+ * copies of shard p into its own arena; then every owner's reduced shard is
+ * copied into the other W-1 arenas.  Movement is device-to-device copies only.
+ *   arenas       HOST array of W device pointers, each to n floats (read and
+ *                written); arenas must not overlap each other
+ *   W            1 <= W <= 16 (W = 1: nothing to do)
+ *   n            elements per arena, >= 0
+ *   stage        device scratch of at least W * ceil(n / W) floats, owned by
+ *                the caller, overwritten; unused (may be NULL) with
+ *                DETFOLD_ROUND_DIRECT
+ *   stage_elems  capacity of `stage` in floats
+ *   flags        DETFOLD_ROUND_REVERSE_DELIVERY: gather the sources' shards
+ *                into the stage in descending source order (slot placement is
+ *                still by source rank, so the bits do not change);
+ *                DETFOLD_ROUND_DIRECT: fold each owner's shard straight from
+ *                the W arenas, with no stage and no gather copies
+ * Errors: DETFOLD_EINVAL, DETFOLD_EOVERLAP (arenas overlap each other or the
+ * stage), DETFOLD_EDEVICE, DETFOLD_ELAUNCH.  Stream-ordered; no synchronize.
+ */
+#define DETFOLD_ROUND_REVERSE_DELIVERY 1
+#define DETFOLD_ROUND_DIRECT 2
+int detfold_loopback_round(float *const *arenas, int32_t W, int64_t n, float *stage,
+                           int64_t stage_elems, int32_t flags, void *stream);
+
+/*
+ * A two-rank all-reduce on one device: the pipeline arm of memra-engine
+ * tests/tp_ar_gpu.rs (ArLink: push the peer partial into staging, order with
+ * events, fold) with each rank a stream.  Rank r pushes its partial into
+ * stage[1-r] by a device copy, and folds x_r += stage[r] once the peer's push
+ * has landed.  All ordering is by events between the two streams; no kernel
+ * spins on a flag, so neither rank can starve the other however much other
+ * work is resident.  The caller owns every buffer, stream and event; the
+ * library keeps no state between calls.
+ */
+typedef struct detfold_pair_link {
+    void *stream[2];  /* hipStream_t of rank 0 and rank 1 (one device; may be equal) */
+    float *stage[2];  /* stage[r]: rank r's staging buffer, capacity floats, device */
+    int64_t capacity; /* floats each staging buffer holds */
+    void *pushed[2];  /* hipEvent_t: recorded on stream[r] after rank r's push */
+    void *folded[2];  /* hipEvent_t: recorded on stream[r] after rank r's fold */
+} detfold_pair_link;
+
+/* Record folded[0] and folded[1] once on their streams before the first
+ * detfold_pair_all_reduce, so the first call's waits have an event to wait for. */
+int detfold_pair_link_init(const detfold_pair_link *link);
+
+/*
+ * detfold_pair_all_reduce -- x0 = x0 + x1 on stream[0] and x1 = x1 + x0 on
+ * stream[1], bit-identical (binary32 addition is commutative), each the
+ * two-addend fold of fold_into.  A call may be repeated on the same link: a
+ * rank refills the peer's staging buffer only after the peer's previous fold
+ * has read it (folded[peer]).
+ *   x0, x1  device pointers to n floats each (read and written)
+ *   n       0 <= n <= capacity
+ * Errors: DETFOLD_EINVAL (NULL link, event, buffer, or n > capacity),
+ * DETFOLD_EOVERLAP (x0, x1, stage[0], stage[1] must be disjoint over n
+ * floats), DETFOLD_EDEVICE, DETFOLD_ELAUNCH.
+ */
+int detfold_pair_all_reduce(const detfold_pair_link *link, float *x0, float *x1, int64_t n);
+
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 3
+#define DETFOLD_ABI_VERSION 4
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 3
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 4
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -264,3 +264,72 @@ def test_shard_plan_rejects_bad_world(detfold_lib):
     a = (ctypes.c_int64 * 2)()
     assert lib.detfold_shard_plan(-1, 2, a, a) == detfold_lib.EINVAL
     assert lib.detfold_shard_plan(5, 2, None, a) == detfold_lib.EINVAL
+
+
+# --------------------------------------------------------------------------
+# separate slots, rounds and the two-stream link: argument checks only
+
+def _ptrs(*addrs):
+    return (ctypes.c_void_p * len(addrs))(*addrs)
+
+
+def test_fold_slots_rejects_bad_arguments(detfold_lib):
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.OK
+    a, b, out = BASE, BASE + (1 << 20), BASE + (1 << 21)
+    assert lib.fold_slots(out, _ptrs(a, b), 0, 16, None) == EINVAL
+    assert lib.fold_slots(out, _ptrs(*[a] * 17), 17, 16, None) == EINVAL   # more than 16 slots
+    assert lib.fold_slots(out, None, 2, 16, None) == EINVAL
+    assert lib.fold_slots(out, _ptrs(a, None), 2, 16, None) == EINVAL
+    assert lib.fold_slots(out, _ptrs(a, b + 2), 2, 16, None) == EINVAL   # misaligned slot
+    assert lib.fold_slots(out + 1, _ptrs(a, b), 2, 16, None) == EINVAL
+    assert lib.fold_slots(out, _ptrs(a, b), 2, -1, None) == EINVAL
+    assert lib.fold_slots(a + 4, _ptrs(a, b), 2, 16, None) == EOVERLAP   # partial overlap with slot 0
+    assert lib.fold_slots(b - 4, _ptrs(a, b), 2, 16, None) == EOVERLAP
+    assert lib.fold_slots_scaled(a + 8, _ptrs(a, b), 2, 16, ctypes.c_float(0.5), None) == EOVERLAP
+    assert lib.fold_slots(None, None, 3, 0, None) == OK                 # nothing to do
+
+
+def test_loopback_round_rejects_bad_arguments(detfold_lib):
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.OK
+    n = 1000
+    ar = [BASE + i * (1 << 20) for i in range(4)]
+    stage = BASE + (1 << 30)
+    need = detfold_lib.round_stage_elems(n, 4)
+    assert need == 1000
+    assert lib.detfold_loopback_round(_ptrs(*ar), 0, n, stage, need, 0, None) == EINVAL
+    assert lib.detfold_loopback_round(_ptrs(*[BASE + i * (1 << 20) for i in range(17)]), 17, n, stage,
+                                      10 ** 6, 0, None) == EINVAL
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, -1, stage, need, 0, None) == EINVAL
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, stage, need, 4, None) == EINVAL     # unknown flag
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, stage, need - 1, 0, None) == EINVAL  # stage short
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, None, 0, 0, None) == EINVAL
+    assert lib.detfold_loopback_round(_ptrs(ar[0], ar[1], ar[1] + 8, ar[3]), 4, n, stage, need, 0,
+                                      None) == EOVERLAP                                   # arenas overlap
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, ar[2] + 100, need, 0, None) == EOVERLAP
+    assert lib.detfold_loopback_round(_ptrs(*ar[:1]), 1, n, None, 0, 0, None) == OK        # one rank
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, 0, None, 0, 0, None) == OK            # empty
+    # direct mode needs no stage, but still checks the arenas
+    assert lib.detfold_loopback_round(_ptrs(ar[0], ar[0], ar[2], ar[3]), 4, n, None, 0,
+                                      detfold_lib.ROUND_DIRECT, None) == EOVERLAP
+
+
+def test_pair_all_reduce_rejects_bad_arguments(detfold_lib):
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.OK
+    link = detfold_lib.PairLinkC()
+    link.capacity = 4096
+    link.stage[0], link.stage[1] = BASE, BASE + (1 << 20)
+    x0, x1 = BASE + (2 << 20), BASE + (3 << 20)
+    assert lib.detfold_pair_all_reduce(None, x0, x1, 16) == EINVAL
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0, x1, 16) == EINVAL      # no events
+    assert lib.detfold_pair_link_init(ctypes.byref(link)) == EINVAL
+    for i in range(2):  # fake event handles: never passed to HIP by the checks below
+        link.pushed[i], link.folded[i] = 0x1000 + i, 0x2000 + i
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0, x1, 4097) == EINVAL    # over capacity
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0, x1, -1) == EINVAL
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0, x0 + 4, 16) == EOVERLAP
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), BASE + 8, x1, 16) == EOVERLAP  # x0 vs stage 0
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0 + 2, x1, 16) == EINVAL  # misaligned
+    assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0, x1, 0) == OK           # nothing to do

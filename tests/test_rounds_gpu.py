@@ -1,0 +1,221 @@
+"""GPU parity for the fold over separate buffers, the one-GPU reduction round
+and the two-stream pair all-reduce (through the C ABI), against the oracle.
+
+* fold_slots: W separate tensors at every 16-byte phase, in place on one of
+  them, with repeated slots (mamba-rs src/dist/reducer.rs: the addends of one
+  owner shard come from W different arenas).
+* loopback_round: W arenas, each owner folds its shard, then distributes it
+  (mamba-rs src/dist/reducer.rs, LoopbackWorld::run_round), staged with
+  ascending and with reversed delivery order (the `reverse_delivery` flag),
+  and direct; every arena must end equal to the oracle's fold of all the
+  arenas, bit for bit.
+* pair all-reduce: two streams as two ranks, push into the peer's reused
+  staging buffer, event-ordered fold (memra-engine tests/tp_ar_gpu.rs, ArLink
+  pipeline arm): sweep n in {1, 4, 1024, 4096, 16384, 65536} and beyond,
+  seeds 11+n / 77+n, the repeat call doubling the sum, and the same beside a
+  stream kept busy with large folds.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import fold_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env(detfold_lib):
+    import torch
+    torch.cuda.init()
+    return detfold_lib, torch, torch.device("cuda:0")
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _assert_bits(got, want, what):
+    g, w = _bits(got), _bits(want)
+    assert g.shape == w.shape, what
+    bad = g != w
+    n_bad = int(np.count_nonzero(bad))
+    if n_bad:
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError("%s: %d of %d words differ; first at %d: got %08x want %08x"
+                             % (what, n_bad, g.size, i, g.flat[i], w.flat[i]))
+
+
+def _host(torch, t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _placed(torch, dev, host, offset):
+    """A device copy of `host` starting `offset` elements into a fresh allocation."""
+    alloc = torch.empty(host.size + 4, dtype=torch.float32, device=dev)
+    view = alloc[offset:offset + host.size]
+    view.copy_(torch.from_numpy(np.ascontiguousarray(host)))
+    return view
+
+
+# --------------------------------------------------------------------------
+# fold over separate buffers
+
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 13, 16])
+@pytest.mark.parametrize("n", [1, 5, 4096, 70001])
+def test_fold_slots_matches_oracle_at_every_phase(env, W, n):
+    df, torch, dev = env
+    host = fold_inputs.slots("mixed", W, n, 31 * W + n)
+    want = oracle.fold([host[r] for r in range(W)])
+    want_s = oracle.fold_stacked_scaled(host, np.float32(0.25))
+    for trial in range(3):
+        offs = [(r * 3 + trial) % 4 for r in range(W)]  # slots at mixed 16-byte phases
+        slots = [_placed(torch, dev, host[r], offs[r]) for r in range(W)]
+        out = _placed(torch, dev, np.full(n, np.nan, np.float32), trial % 4)
+        _say("case: fold_slots W=%d n=%d offsets %s" % (W, n, offs))
+        df.fold_slots(out, slots)
+        _assert_bits(_host(torch, out), want, "fold_slots W=%d n=%d offsets %s" % (W, n, offs))
+        df.fold_slots_scaled(out, slots, 0.25)
+        _assert_bits(_host(torch, out), want_s, "fold_slots_scaled W=%d n=%d" % (W, n))
+
+
+@pytest.mark.parametrize("W", [2, 5, 8, 16])
+def test_fold_slots_in_place_and_repeated_slots(env, W):
+    df, torch, dev = env
+    n = 100_003
+    host = fold_inputs.slots("varied", W, n, 900 + W, spread=4.0)
+    want = oracle.fold([host[r] for r in range(W)])
+    for k in (0, W - 1):  # out is slot k
+        slots = [_placed(torch, dev, host[r], r % 4) for r in range(W)]
+        df.fold_slots(slots[k], slots)
+        _assert_bits(_host(torch, slots[k]), want, "in place on slot %d, W=%d" % (k, W))
+    # the same buffer passed as two slots folds it twice, in order
+    a = _placed(torch, dev, host[0], 1)
+    b = _placed(torch, dev, host[1], 0)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    df.fold_slots(out, [a, b, a])
+    _assert_bits(_host(torch, out), oracle.fold([host[0], host[1], host[0]]), "repeated slot")
+
+
+# --------------------------------------------------------------------------
+# the one-GPU reduction round
+
+ROUND_CASES = [(2, 1), (2, 10_007), (3, 7), (8, 3), (8, 10_007), (8, 1 << 20), (16, 10_000_019),
+               (16, 99_991), (5, 3_000_001)]
+
+
+@pytest.mark.parametrize("W,n", ROUND_CASES)
+def test_loopback_round_every_arena_holds_the_fold(env, W, n):
+    df, torch, dev = env
+    host = fold_inputs.slots("vecf" if W in (8, 16) else "mixed", W, n, 3000 + 7 * W)
+    want = oracle.fold_stacked(host)
+    stage = torch.empty(df.round_stage_elems(n, W) + 1, dtype=torch.float32, device=dev)
+    for mode in ("ascending", "reversed", "direct"):
+        _say("case: loopback round W=%d n=%d %s" % (W, n, mode))
+        # arenas at mixed 16-byte phases, each in its own allocation
+        arenas = [_placed(torch, dev, host[r], (r + n) % 4) for r in range(W)]
+        df.loopback_round(arenas, None if mode == "direct" else stage[1:],
+                          reverse_delivery=(mode == "reversed"), direct=(mode == "direct"))
+        for r in range(W):
+            _assert_bits(_host(torch, arenas[r]), want, "W=%d n=%d %s arena %d" % (W, n, mode, r))
+
+
+def test_loopback_round_twice_doubles(env):
+    # after one round every arena holds S; a second round over W copies of S
+    # folds S W times in ascending order
+    df, torch, dev = env
+    W, n = 4, 65_537
+    host = fold_inputs.slots("vecf", W, n, 77)
+    s = oracle.fold_stacked(host)
+    arenas = [_placed(torch, dev, host[r], 0) for r in range(W)]
+    df.loopback_round(arenas, direct=True)
+    df.loopback_round(arenas, direct=True)
+    want = oracle.fold([s] * W)
+    for r in range(W):
+        _assert_bits(_host(torch, arenas[r]), want, "second round arena %d" % r)
+
+
+def test_loopback_round_one_rank_is_a_no_op(env):
+    df, torch, dev = env
+    host = fold_inputs.vecf(1000, 1)
+    a = _placed(torch, dev, host, 0)
+    df.loopback_round([a])
+    _assert_bits(_host(torch, a), host, "W=1 round")
+
+
+# --------------------------------------------------------------------------
+# two ranks on two streams
+
+def _pair_round(df, torch, link, xa, xb):
+    link.all_reduce(xa, xb)
+    for st in link.streams:
+        st.synchronize()
+
+
+def test_pair_all_reduce_sweep_doubles_on_repeat(env):
+    df, torch, dev = env
+    link = df.PairLink(1 << 18, device=dev)  # staging reused by every size and call
+    for n in (1, 4, 1024, 4096, 16384, 65536, 1 << 18):
+        _say("case: pair all-reduce n=%d" % n)
+        ha, hb = fold_inputs.vecf(n, 11 + n), fold_inputs.vecf(n, 77 + n)
+        want = oracle.fold_into(ha, hb)
+        xa = torch.from_numpy(ha).to(dev)
+        xb = torch.from_numpy(hb).to(dev)
+        torch.cuda.synchronize()
+        _pair_round(df, torch, link, xa, xb)
+        _assert_bits(xa.cpu().numpy(), want, "rank 0 n=%d" % n)
+        _assert_bits(xb.cpu().numpy(), want, "rank 1 n=%d" % n)
+        _pair_round(df, torch, link, xa, xb)
+        twice = oracle.fold_into(want, want)
+        _assert_bits(xa.cpu().numpy(), twice, "rank 0 second call n=%d" % n)
+        _assert_bits(xb.cpu().numpy(), twice, "rank 1 second call n=%d" % n)
+
+
+def test_pair_all_reduce_back_to_back_without_host_sync(env):
+    # ten calls queued with no synchronization between them: the events alone
+    # keep each push from overwriting a staging buffer the peer still reads
+    df, torch, dev = env
+    n = 65536
+    link = df.PairLink(n, device=dev)
+    ha, hb = fold_inputs.varied(n, 3, 1.0), fold_inputs.varied(n, 4, 1.0)
+    xa = torch.from_numpy(ha).to(dev)
+    xb = torch.from_numpy(hb).to(dev)
+    torch.cuda.synchronize()
+    want = oracle.fold_into(ha, hb)
+    for _ in range(10):
+        link.all_reduce(xa, xb)
+        want = oracle.fold_into(want, want) if _ else want
+    for st in link.streams:
+        st.synchronize()
+    _assert_bits(xa.cpu().numpy(), want, "rank 0 after 10 calls")
+    _assert_bits(xb.cpu().numpy(), want, "rank 1 after 10 calls")
+
+
+def test_pair_all_reduce_beside_a_busy_stream(env):
+    df, torch, dev = env
+    big = torch.from_numpy(fold_inputs.slots("vecf", 8, 1 << 22, 5)).to(dev)
+    big_out = torch.empty(1 << 22, dtype=torch.float32, device=dev)
+    n = 1 << 16
+    link = df.PairLink(n, device=dev)
+    ha, hb = fold_inputs.vecf(n, 11 + n), fold_inputs.vecf(n, 77 + n)
+    xa = torch.from_numpy(ha).to(dev)
+    xb = torch.from_numpy(hb).to(dev)
+    torch.cuda.synchronize()
+    busy = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(busy):
+        for _ in range(30):
+            df.fold_ranks(big_out, big)
+    link.all_reduce(xa, xb)
+    for st in link.streams:
+        st.synchronize()
+    _assert_bits(xa.cpu().numpy(), oracle.fold_into(ha, hb), "rank 0 beside a busy stream")
+    _assert_bits(xb.cpu().numpy(), oracle.fold_into(ha, hb), "rank 1 beside a busy stream")
+    busy.synchronize()
