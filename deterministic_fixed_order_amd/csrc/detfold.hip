@@ -782,6 +782,7 @@ int run_ranks(float *out, const float *stacked, int32_t W, int64_t len, bool sca
 // thread, one pass, no cache hints.  Larger payloads are bandwidth bound and
 // take the streaming policy.
 constexpr int64_t kLatencyBytes = 8 << 20;
+constexpr int64_t kCopyCachedBytes = 1 << 20;
 
 int plan_into(const Geometry &g, int32_t cu_count, detfold_plan *p)
 {
@@ -851,8 +852,8 @@ int run_slots(float *out, const float *const *slots, int32_t W, int64_t len, boo
 }
 
 // Copy len floats from src to each of ndst destinations with k_copy_out.
-// Payloads up to kLatencyBytes take no cache hints (they are read again
-// soon); larger ones stream.  One pass of 256-thread workgroups, capped at 8
+// Payloads up to kCopyCachedBytes take no cache hints (a decode-join push is
+// read by the peer's fold right away); larger ones stream.  One pass of 256-thread workgroups, capped at 8
 // per CU with the rest covered by the grid-stride loop.
 int copy_out(float *const *dsts, int ndst, const float *src, int64_t len, int32_t cu,
              hipStream_t stream, hipEvent_t done = nullptr)
@@ -877,7 +878,7 @@ int copy_out(float *const *dsts, int ndst, const float *src, int64_t len, int32_
         grid = cap;
     if (grid < 1)
         grid = 1;
-    const bool stream_pol = len * 4 > kLatencyBytes;
+    const bool stream_pol = len * 4 > kCopyCachedBytes;
     const void *k = vec ? (stream_pol ? (const void *)k_copy_out<true, kStream> : (const void *)k_copy_out<true, kCached>)
                         : (stream_pol ? (const void *)k_copy_out<false, kStream> : (const void *)k_copy_out<false, kCached>);
     void *args[] = {&t, &ndst, &src, &len, &head};

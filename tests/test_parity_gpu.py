@@ -482,3 +482,27 @@ def test_graph_replays_match_eager(env):
         eager = torch.empty_like(out)
         df.fold_ranks(eager, stacked)  # eager work between replays
         _assert_bits(_host(eager), want, "eager between replays %d" % rep)
+
+
+def test_lengths_beyond_int32(env):
+    """The pages' kernel took an i32 length; here len is 64-bit.  A W=2 fold of
+    2^31 + 13 elements per slot (8 GiB each), checked on sampled outputs: 2^20
+    random positions, the last 100 and the 113 around 2^31."""
+    df, torch, dev = env
+    n = (1 << 31) + 13
+    _say("case: W=2 len=2^31+13 (16 GiB of addends)")
+    host = fold_inputs.slots("vecf", 2, n, 555)
+    stacked = torch.empty((2, n), dtype=torch.float32, device=dev)
+    for r in range(2):
+        stacked[r].copy_(torch.from_numpy(host[r]))
+    rng = np.random.default_rng(5)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(n - 100, n),
+                                    np.arange((1 << 31) - 100, (1 << 31) + 13)]))
+    want = oracle.fold([host[0][idx], host[1][idx]])
+    idx_dev = torch.from_numpy(idx).to(dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    df.fold_ranks(out, stacked)
+    _assert_bits(_host(out[idx_dev]), want, "fold_ranks at 2^31+13")
+    del out
+    df.fold_into(stacked[0], stacked[1])  # in place, streaming path
+    _assert_bits(_host(stacked[0][idx_dev]), want, "fold_into at 2^31+13")
