@@ -1,0 +1,77 @@
+"""Ranks as processes on one GPU (mamba-rs src/dist/reducer.rs: the owner-shard
+dataflow of reduce_sum_fixed_order_nccl, with the process boundary the
+transport path has).
+
+Each of W processes (W = 2 or 4) is a rank owning one arena; the arenas are
+shared between the processes through device memory handles (torch's IPC
+sharing of device tensors).  Rank r folds its owner shard in place, reading the other ranks' arenas
+directly through the mapped handles (fold_slots over [arena_0, ...] at the
+shard), then writes its reduced shard into the other ranks' arenas.  A CPU barrier
+(gloo, host-side only) separates the phases.  Every arena must end equal to the
+oracle's fold of the original arenas, bit for bit.
+"""
+import os
+import socket
+
+import numpy as np
+import pytest
+
+import fold_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _free_port():
+    with socket.socket(socket.AF_INET, socket.SOCK_STREAM) as s:
+        s.bind(("127.0.0.1", 0))
+        return s.getsockname()[1]
+
+
+def _rank_main(rank, arenas, n, port, world):
+    import sys
+    import torch
+    import torch.distributed as dist
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import deterministic_fixed_order_amd as df
+
+    os.environ["MASTER_ADDR"] = "127.0.0.1"
+    os.environ["MASTER_PORT"] = str(port)
+    dist.init_process_group("gloo", rank=rank, world_size=world)
+    try:
+        torch.cuda.set_device(0)
+        start, length = df.shard_plan(n, world)[rank]
+        mine = arenas[rank]
+        if length:
+            # phase A: fold my owner shard from every rank's arena, in place
+            df.fold_slots(mine[start:start + length], [a[start:start + length] for a in arenas])
+        torch.cuda.synchronize()
+        dist.barrier()
+        # phase B: my reduced shard goes into every other rank's arena (byte movement)
+        if length:
+            for p, a in enumerate(arenas):
+                if p != rank:
+                    a[start:start + length].copy_(mine[start:start + length])
+        torch.cuda.synchronize()
+        dist.barrier()
+    finally:
+        dist.destroy_process_group()
+
+
+@pytest.mark.parametrize("world,n", [(2, 1), (2, 1001), (2, 1 << 20), (4, 3), (4, 1 << 20)])
+def test_processes_fold_through_shared_arenas(detfold_lib, world, n):
+    import torch
+    import torch.multiprocessing as mp
+
+    host = fold_inputs.slots("varied", world, n, 8800 + n, spread=2.0)
+    want = oracle.fold_stacked(host)
+    dev = torch.device("cuda:0")
+    arenas = [torch.from_numpy(host[r]).to(dev) for r in range(world)]
+    torch.cuda.synchronize()
+    print("case: %d processes, n=%d" % (world, n), flush=True)
+    mp.spawn(_rank_main, args=(arenas, n, _free_port(), world), nprocs=world, join=True)
+    for r in range(world):
+        got = arenas[r].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
