@@ -54,9 +54,37 @@ WORKLOAD_NAMES = {
 }
 
 
+def code_text(src: str) -> str:
+    """The C++ source with comments removed and whitespace runs collapsed, so
+    that the hash below changes with the code, not with its commentary.
+    String and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code (comments and layout excluded)."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def log(msg: str) -> None:
@@ -211,10 +239,8 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
     p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
     if p["path"] == df.PATH_ROWS:
-        aligned = (out.data_ptr() - stacked.data_ptr()) % 16 == 0 and (W <= 2 or n % 4 == 0) \
-            and (W < 2 or (out.data_ptr() - stacked.data_ptr() - 4 * n) % 16 == 0)
-        return "k_fold_rows<%d,%s,%s> grid=%d block=%d tile=%d" % (
-            W, str(aligned).lower(), str(scaled).lower(), p["grid"], p["block"], p["tile"])
+        return "k_fold_rows<%d,%s> grid=%d block=%d tile=%d" % (
+            W, str(scaled).lower(), p["grid"], p["block"], p["tile"])
     body = "k_fold_vector" if p["path"] == df.PATH_VECTOR else "k_fold_scalar"
     ws = W if W in (1, 2, 4, 8, 16) else 0
     pol = 1 if p["policy"] == df.POLICY_STREAM else 0
@@ -371,6 +397,7 @@ def bench_pair(args, torch, df, dev):
     import fold_inputs
 
     link = df.PairLink(max(JOIN_SIZES), device=dev)
+    shot = df.OneShotLink(max(JOIN_SIZES), device=dev, stream=torch.cuda.Stream(device=dev))
     rows = []
     for n in JOIN_SIZES:
         xa = torch.from_numpy(fold_inputs.vecf(n, 11 + n)).to(dev)
@@ -392,10 +419,15 @@ def bench_pair(args, torch, df, dev):
             for st in link.streams:
                 st.synchronize()
             one.append((time.perf_counter() - t1) * 1e6)
-        rows.append({"n": n, "back_to_back_us_per_call": round(b2b, 3),
-                     "enqueue_to_complete_us_median": round(statistics.median(one), 3)})
-        log("pair all-reduce n=%6d: %.2f us/call back-to-back, %.2f us call+sync"
-            % (n, b2b, statistics.median(one)))
+        row = {"n": n, "back_to_back_us_per_call": round(b2b, 3),
+               "enqueue_to_complete_us_median": round(statistics.median(one), 3)}
+        row["one_shot"] = bench_one_shot(torch, df, dev, shot, xa, xb)
+        rows.append(row)
+        log("pair all-reduce n=%6d: %.2f us/call back-to-back, %.2f us call+sync; one-shot %s"
+            % (n, b2b, statistics.median(one), row["one_shot"]))
+    words = shot.barrier_words()
+    if words != [0, 0]:
+        raise RuntimeError("one-shot barrier words %s after the sweep" % words)
     at16 = next(r for r in rows if r["n"] == 4096)
     return {
         "metric": "two-stream pair all-reduce at 16 KiB (enqueue to completion)",
@@ -405,6 +437,47 @@ def bench_pair(args, torch, df, dev):
         "data": "synthetic", "config": {"workload": WORKLOAD_NAMES["pair"], "n": 4096},
         "pair": rows,
     }
+
+
+def bench_one_shot(torch, df, dev, shot, xa, xb):
+    """The one-kernel all-reduce on the same buffers: back-to-back through the
+    binding, one call with a host synchronization, and 200 calls captured in
+    one HIP graph (device time per call)."""
+    st = shot.stream
+    for _ in range(20):
+        shot.all_reduce(xa, xb)
+    st.synchronize()
+    reps = 500
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        shot.all_reduce(xa, xb)
+    st.synchronize()
+    b2b = (time.perf_counter() - t0) / reps * 1e6
+    one = []
+    for _ in range(200):
+        t1 = time.perf_counter()
+        shot.all_reduce(xa, xb)
+        st.synchronize()
+        one.append((time.perf_counter() - t1) * 1e6)
+    k_graph = 200
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for _ in range(k_graph):
+            shot.all_reduce(xa, xb)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream(dev)
+    ev0.record(cur)
+    for _ in range(10):
+        graph.replay()
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    in_graph = ev0.elapsed_time(ev1) * 1e3 / (10 * k_graph)
+    del graph
+    return {"back_to_back_us_per_call": round(b2b, 3),
+            "enqueue_to_complete_us_median": round(statistics.median(one), 3),
+            "graph_replay_us_per_call": round(in_graph, 3)}
 
 
 def sweep(args, torch, df, dev):

@@ -15,6 +15,8 @@ PyTorch is used for device memory and streams only.
     fold_slots(out, [s_0, ..., s_{W-1}])     the fold over separate buffers (W <= 16)
     loopback_round(arenas, stage=None, ...)  one owner-shard reduction round over W arenas
     PairLink(...).all_reduce(x0, x1)         two-stream (two-rank) all-reduce on one device
+    PairLink(...).broadcast / all_gather     pure movement between the two ranks
+    OneShotLink(...).all_reduce(x0, x1)      the one-kernel arm with an in-kernel barrier
 
 ``stacked`` is a ``[W, len]`` float32 CUDA/HIP tensor (row r = slot r); a view
 with a storage offset is fine as long as it is contiguous.
@@ -31,14 +33,19 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 4
+ABI_VERSION = 5
+ONE_SHOT_BLOCKS = 64
+ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
+BARRIER_ENTRY_EXPIRED, BARRIER_EXIT_EXPIRED = 40043, 40044
 ROUND_REVERSE_DELIVERY, ROUND_DIRECT = 1, 2
 
 EXPORTS = (
     "fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror", "detfold_abi_version",
     "detfold_shard_plan", "detfold_plan_fold_ranks", "detfold_plan_fold_into",
     "detfold_fold_ranks_ex", "fold_slots", "fold_slots_scaled", "detfold_loopback_round",
-    "detfold_pair_link_init", "detfold_pair_all_reduce",
+    "detfold_pair_link_init", "detfold_pair_all_reduce", "detfold_pair_broadcast",
+    "detfold_pair_all_gather", "detfold_one_shot_init", "detfold_one_shot_all_reduce",
+    "detfold_one_shot_rank",
 )
 
 
@@ -57,6 +64,12 @@ class PairLinkC(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p * 2), ("stage", ctypes.c_void_p * 2),
                 ("capacity", ctypes.c_int64), ("pushed", ctypes.c_void_p * 2),
                 ("folded", ctypes.c_void_p * 2)]
+
+
+class OneShotLinkC(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("stage", ctypes.c_void_p * 2),
+                ("capacity", ctypes.c_int64), ("flags", ctypes.c_void_p), ("words", ctypes.c_void_p),
+                ("spin_limit", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -102,11 +115,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.detfold_loopback_round.argtypes = [pp, i32, i64, f32p, i64, i32, vp]
     lib.detfold_pair_link_init.argtypes = [ctypes.POINTER(PairLinkC)]
     lib.detfold_pair_all_reduce.argtypes = [ctypes.POINTER(PairLinkC), f32p, f32p, i64]
-    for name in ("fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_fold_ranks_ex",
-                 "detfold_abi_version", "detfold_shard_plan", "detfold_plan_fold_ranks",
-                 "detfold_plan_fold_into", "fold_slots", "fold_slots_scaled",
-                 "detfold_loopback_round", "detfold_pair_link_init", "detfold_pair_all_reduce"):
-        getattr(lib, name).restype = ctypes.c_int
+    lib.detfold_pair_broadcast.argtypes = [ctypes.POINTER(PairLinkC), i32, f32p, f32p, i64]
+    lib.detfold_pair_all_gather.argtypes = [ctypes.POINTER(PairLinkC), f32p, f32p, f32p, f32p, i64]
+    lib.detfold_one_shot_init.argtypes = [ctypes.POINTER(OneShotLinkC)]
+    lib.detfold_one_shot_all_reduce.argtypes = [ctypes.POINTER(OneShotLinkC), f32p, f32p, i64]
+    lib.detfold_one_shot_rank.argtypes = [ctypes.POINTER(OneShotLinkC), i32, f32p, i64, vp]
+    for name in EXPORTS:
+        if name != "detfold_strerror":
+            getattr(lib, name).restype = ctypes.c_int
     if lib.detfold_abi_version() != ABI_VERSION:
         raise RuntimeError("libdetfold ABI mismatch")
     _lib = lib
@@ -286,6 +302,76 @@ class PairLink:
             raise ValueError("x0 has %d elements, x1 %d" % (x0.numel(), x1.numel()))
         _check(load().detfold_pair_all_reduce(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
                                               x0.numel()), "pair_all_reduce")
+
+    def broadcast(self, root: int, src, dst) -> None:
+        """``dst`` (rank ``1 - root``) becomes a byte copy of ``src`` (rank ``root``)."""
+        _f32_device(src, "src")
+        _f32_device(dst, "dst")
+        if src.numel() != dst.numel():
+            raise ValueError("src has %d elements, dst %d" % (src.numel(), dst.numel()))
+        _check(load().detfold_pair_broadcast(ctypes.byref(self._c), int(root), src.data_ptr(),
+                                             dst.data_ptr(), src.numel()), "pair_broadcast")
+
+    def all_gather(self, x0, x1, f0, f1) -> None:
+        """``f0`` and ``f1`` (2 * span floats) both become ``[x0 | x1]``."""
+        for t, nm in ((x0, "x0"), (x1, "x1"), (f0, "f0"), (f1, "f1")):
+            _f32_device(t, nm)
+        span = x0.numel()
+        if x1.numel() != span or f0.numel() != 2 * span or f1.numel() != 2 * span:
+            raise ValueError("all_gather needs x0, x1 of one span and f0, f1 of twice it")
+        _check(load().detfold_pair_all_gather(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
+                                              f0.data_ptr(), f1.data_ptr(), span), "pair_all_gather")
+
+
+class OneShotLink:
+    """The one-kernel two-rank all-reduce (the library's ``detfold_one_shot_link``):
+    staging buffers, device barrier counters and two barrier words.
+
+    ``all_reduce(x0, x1)`` runs both ranks in one launch; ``rank(r, x)`` runs
+    rank r's kernel alone (both ranks must then be launched, with the same n).
+    ``barrier_words()`` reads the two words: 0, or ``BARRIER_ENTRY_EXPIRED`` /
+    ``BARRIER_EXIT_EXPIRED`` when a wait ran out of polls."""
+
+    def __init__(self, capacity: int, device=None, stream=None, spin_limit: int = 0):
+        import torch
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        self.stage = [torch.empty(max(capacity, 1), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.flags = torch.empty(ONE_SHOT_FLAG_WORDS, dtype=torch.int32, device=dev)
+        self.words = torch.empty(2, dtype=torch.int32, device=dev)
+        self.capacity = capacity
+        self._c = OneShotLinkC()
+        self._c.stream = self.stream.cuda_stream
+        for r in range(2):
+            self._c.stage[r] = self.stage[r].data_ptr()
+        self._c.capacity = capacity
+        self._c.flags = self.flags.data_ptr()
+        self._c.words = self.words.data_ptr()
+        self._c.spin_limit = spin_limit
+        self.init()
+
+    def init(self) -> None:
+        """Zero the counters and words (synchronizes the link's stream)."""
+        _check(load().detfold_one_shot_init(ctypes.byref(self._c)), "one_shot_init")
+
+    def all_reduce(self, x0, x1) -> None:
+        _f32_device(x0, "x0")
+        _f32_device(x1, "x1")
+        if x0.numel() != x1.numel():
+            raise ValueError("x0 has %d elements, x1 %d" % (x0.numel(), x1.numel()))
+        _check(load().detfold_one_shot_all_reduce(ctypes.byref(self._c), x0.data_ptr(),
+                                                  x1.data_ptr(), x0.numel()), "one_shot_all_reduce")
+
+    def rank(self, r: int, x, stream=None) -> None:
+        _f32_device(x, "x")
+        _check(load().detfold_one_shot_rank(ctypes.byref(self._c), int(r), x.data_ptr(), x.numel(),
+                                            _stream_handle(x, stream)), "one_shot_rank")
+
+    def barrier_words(self) -> list:
+        import torch
+        torch.cuda.synchronize(self.device)
+        return [int(v) for v in self.words.cpu().tolist()]
 
 
 def shard_plan(n: int, world: int) -> list[tuple[int, int]]:

@@ -17,15 +17,19 @@
 //    add, so the adds wait on data, not the reverse.  `unroll` groups per thread
 //    per pass multiply the bytes in flight.
 //  * When `out` and the slots sit at different offsets modulo 16 bytes no
-//    element index lines them all up, so the scalar body gives each lane one
-//    4-byte element per slot (a wave still reads 256 contiguous bytes per
-//    slot).  Loads are pure data movement: the chain, and so the bits, is the
-//    same on either body.
+//    element index lines them all up.  The LDS row body (2 <= W <= 16) still
+//    moves 16-byte blocks: each wave's buffer descriptor starts at its own
+//    slot's first element of the tile.  The direct bodies give each lane one
+//    4-byte element per slot instead (a wave still reads 256 contiguous bytes
+//    per slot).  Loads are pure data movement: the chain, and so the bits, is
+//    the same on every body.
 //  * A grid-stride loop lets any grid cover any length; the default grid is
 //    sized from the device's compute-unit count.
-//  * No atomics, no flags, no waits on other work: a launch completes on its
-//    own, whatever else is resident (the latency path of fold_into relies on
-//    this).
+//  * The fold kernels have no atomics, no flags and no waits on other work: a
+//    launch completes on its own, whatever else is resident (the latency path
+//    of fold_into relies on this).  The one-shot all-reduce kernel is the only
+//    code that waits on another workgroup, and every one of its waits is
+//    bounded by a poll count.
 //  * Compiled with -ffp-contract=off, no fast-math, packed-FP32 instructions
 //    disabled, and f32 denormals enabled (the HIP default on gfx9), so every
 //    add is a single v_add_f32 under IEEE round-to-nearest-even.
@@ -259,14 +263,15 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
 // rows; the direct body instead has every wave touch W runs 1 KiB at a time,
 // which measured 3-8% slower on MI355X.
 //
-// Slot phases: the tile of `out` starts 16-byte aligned; slot r's bytes for
-// the tile start delta_r = (phase(slot r) - phase(out)) mod 4 dwords past a
-// 16-byte boundary.  ALIGNED (every delta_r = 0): row r holds the tile
-// exactly.  Otherwise wave r loads the 16-byte blocks covering the tile's
-// bytes -- at most one block more, starting at most 12 bytes before them, and
-// never leaving the 16-byte blocks that hold the slot's first and last
-// elements -- and the fold reads each element at dword delta_r + 4t + k of
-// row r.  The bits are those of the per-element chain either way.
+// Slot phases: the tile of `out` starts 16-byte aligned, but slot r's bytes
+// for the tile may start at any dword.  Wave r's buffer descriptor is based at
+// exactly that dword (gfx9 buffer loads need only dword alignment), so every
+// row lands in LDS aligned to the tile whatever the slot's phase, and the
+// fold reads 16-byte groups from every row alike.  The descriptor's range is
+// the tile's bytes of the slot, so no lane reads past them.  Measured on
+// MI355X against realigning shifted rows in LDS (one extra KiB loaded per
+// wave, 4-byte LDS reads): +3% at W=16 x 10,000,019 at base+1, +10% at W=7,
+// no change when every slot is aligned.
 template <int W> struct RowsShape {
     static constexpr int LPW = rows_kib_per_wave(W);  // KiB each wave streams per tile
     static constexpr int T = LPW * 64;                // 16-byte groups per tile
@@ -294,14 +299,12 @@ __device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slot
     out[i] = acc;
 }
 
-template <int W, bool ALIGNED, bool SCALED>
+template <int W, bool SCALED>
 __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
                                                       int64_t head, float inv_w)
 {
     constexpr int LPW = RowsShape<W>::LPW, T = RowsShape<W>::T;
-    constexpr int LOADS = ALIGNED ? LPW : LPW + 1;  // one more block when the slot is shifted
-    constexpr int ROW = LOADS * 64;                 // groups per LDS row
-    __shared__ f4 rows[W][ROW];
+    __shared__ f4 rows[W][T];
 
     const int64_t groups = (len - head) >> 2;
     const int64_t tail0 = head + (groups << 2);
@@ -316,12 +319,9 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slot
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;  // first element of the tile; out + e0 is 16-byte aligned
-        const uintptr_t first = (uintptr_t)(slot + e0);
-        const uintptr_t lo = first & ~(uintptr_t)15;
-        const uintptr_t hi = ((uintptr_t)(slot + e0 + 4 * cnt) + 15) & ~(uintptr_t)15;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void *)lo, (uint32_t)(hi - lo));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot + e0, (uint32_t)(cnt * 16));
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u)
+        for (int u = 0; u < LPW; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
                                                      (uint32_t)(u * 64 + lane) * 16u, 0, 0,
                                                      Aux<kStream>::load);
@@ -329,21 +329,10 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slot
 
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + e0, (uint32_t)(cnt * 16));
         for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += W * 64) {
-            f4 acc;
-            if constexpr (ALIGNED) {
-                acc = rows[0][t];
+            f4 acc = rows[0][t];
 #pragma unroll
-                for (int q = 1; q < W; ++q)
-                    acc = acc + rows[q][t];  // ascending slot order, one rounding per add
-            } else {
-#pragma unroll
-                for (int q = 0; q < W; ++q) {
-                    const uint32_t d = (uint32_t)(((uintptr_t)(slots.p[q] + e0) >> 2) & 3);
-                    const float *row = reinterpret_cast<const float *>(&rows[q][0]) + d + 4 * t;
-                    const f4 v = {row[0], row[1], row[2], row[3]};
-                    acc = q == 0 ? v : acc + v;
-                }
-            }
+            for (int q = 1; q < W; ++q)
+                acc = acc + rows[q][t];  // ascending slot order, one rounding per add
             if constexpr (SCALED)
                 acc = acc * inv_w;  // one rounding of the finished sum
             bstore<Aux<kStream>::store>(acc, ro, t * 16u);
@@ -394,6 +383,123 @@ __global__ __launch_bounds__(kMaxBlock) void k_copy_out(SlotTable dsts, int ndst
                 const_cast<float *>(dsts.p[d])[i] = v;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// One-shot two-rank all-reduce (memra-engine tests/tp_ar_gpu.rs, the one-shot
+// arm: one kernel per rank, an in-kernel barrier with entry and exit refusal
+// words, repeat calls on the same link).
+//
+// Workgroup b of rank r owns chunk b of the payload and pairs with workgroup b
+// of the peer; the two meet through four counters per pair (entry and exit,
+// one per rank).  A workgroup arrives by incrementing its own counter and
+// waits until the peer's counter has caught up with the value it produced.
+// Neither side can run a whole call ahead: the peer's next arrival at entry
+// follows its exit wait, which needs this side's exit arrival.  Counters only
+// ever grow, so a call needs no epoch from the host and a graph replay of a
+// captured call is a fresh call.
+
+constexpr int kOneShotBlock = 256;
+constexpr int64_t kOneShotPerBlock = 1024;  // payload floats per workgroup before the cap
+constexpr int32_t kDefaultSpinLimit = 1 << 20;
+
+struct OneShotArgs {
+    float *x[2];      // the ranks' partials, folded in place
+    float *stage[2];  // stage[r]: where the peer's partial lands for rank r
+    uint32_t *flags;  // [entry|exit][rank][DETFOLD_ONE_SHOT_BLOCKS] counters
+    int32_t *words;   // per-rank barrier word
+    int64_t n;
+    int64_t chunk;    // floats per workgroup, a multiple of 4
+    int32_t blocks;   // workgroups per rank
+    int32_t rank0;    // rank of workgroups [0, blocks); a two-rank launch adds rank 1 after them
+    int32_t spin_limit;
+    int32_t vec;      // every buffer 16-byte aligned: 16-byte accesses
+};
+
+// Poll *f (agent scope, acquire) until it reaches `target`, at most `limit`
+// times.  Signed distance, so the comparison survives counter wrap.
+__device__ bool await_count(const uint32_t *f, uint32_t target, int32_t limit)
+{
+    for (int32_t i = 0; i < limit; ++i) {
+        const uint32_t v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int32_t)(v - target) >= 0)
+            return true;
+        __builtin_amdgcn_s_sleep(4);
+    }
+    return false;
+}
+
+// Arrive at a barrier: bump this workgroup's counter with an agent-scope
+// release, which writes the L2 back before the increment lands, so the
+// workgroup's stores (ordered before it by the caller's __syncthreads) are
+// visible to the peer's acquire on any XCD.  Returns the count produced.
+__device__ uint32_t arrive(uint32_t *f)
+{
+    return __hip_atomic_fetch_add(f, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+
+// Keep the first refusal word stored for a rank.
+__device__ void refuse(int32_t *word, int32_t code)
+{
+    int32_t expected = 0;
+    __hip_atomic_compare_exchange_strong(word, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kOneShotBlock) void k_one_shot(OneShotArgs a)
+{
+    __shared__ int passed;
+    const int32_t rank = a.rank0 + (int32_t)blockIdx.x / a.blocks;
+    const int32_t b = (int32_t)blockIdx.x % a.blocks;
+    const int32_t peer = 1 - rank;
+    uint32_t *const entry = a.flags;
+    uint32_t *const exit = a.flags + 2 * DETFOLD_ONE_SHOT_BLOCKS;
+    const int64_t lo = (int64_t)b * a.chunk;
+    const int64_t hi = lo + a.chunk < a.n ? lo + a.chunk : a.n;
+    const int64_t len = hi > lo ? hi - lo : 0;
+    float *const x = a.x[rank] + lo;
+    float *const push = a.stage[peer] + lo;
+    const float *const mine = a.stage[rank] + lo;
+    const int64_t groups = a.vec ? len >> 2 : 0;
+
+    // 1. this rank's chunk goes to the peer's staging buffer
+    for (int64_t g = threadIdx.x; g < groups; g += kOneShotBlock)
+        reinterpret_cast<f4 *>(push)[g] = reinterpret_cast<const f4 *>(x)[g];
+    for (int64_t i = (groups << 2) + threadIdx.x; i < len; i += kOneShotBlock)
+        push[i] = x[i];
+    __syncthreads();
+    // 2. entry barrier: the peer's chunk has landed in stage[rank]
+    if (threadIdx.x == 0) {
+        const uint32_t mine_count = arrive(entry + rank * DETFOLD_ONE_SHOT_BLOCKS + b);
+        const bool ok = await_count(entry + peer * DETFOLD_ONE_SHOT_BLOCKS + b, mine_count, a.spin_limit);
+        if (!ok)
+            refuse(a.words + rank, DETFOLD_BARRIER_ENTRY_EXPIRED);
+        passed = ok;
+    }
+    __syncthreads();
+    if (!passed)
+        return;
+    // 3. the fold, x_r + x_peer
+    for (int64_t g = threadIdx.x; g < groups; g += kOneShotBlock) {
+        const f4 v = reinterpret_cast<const f4 *>(x)[g] + reinterpret_cast<const f4 *>(mine)[g];
+        reinterpret_cast<f4 *>(x)[g] = v;
+    }
+    for (int64_t i = (groups << 2) + threadIdx.x; i < len; i += kOneShotBlock)
+        x[i] = x[i] + mine[i];
+    __syncthreads();
+    // 4. exit barrier: the peer has finished reading the stage this rank refills next call
+    if (threadIdx.x == 0) {
+        const uint32_t mine_count = arrive(exit + rank * DETFOLD_ONE_SHOT_BLOCKS + b);
+        if (!await_count(exit + peer * DETFOLD_ONE_SHOT_BLOCKS + b, mine_count, a.spin_limit))
+            refuse(a.words + rank, DETFOLD_BARRIER_EXIT_EXPIRED);
+    }
+}
+
+__global__ __launch_bounds__(kOneShotBlock) void k_zero_words(uint32_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -659,31 +765,25 @@ scalar_kernel_t pick_scalar_w(int unroll, int policy)
 
 typedef void (*rows_kernel_t)(float *, SlotTable, int64_t, int64_t, float);
 
-template <int W, bool SCALED>
-rows_kernel_t pick_rows_w(bool aligned)
-{
-    return aligned ? k_fold_rows<W, true, SCALED> : k_fold_rows<W, false, SCALED>;
-}
-
 template <bool SCALED>
-rows_kernel_t pick_rows(int32_t w, bool aligned)
+rows_kernel_t pick_rows(int32_t w)
 {
     switch (w) {
-    case 2: return pick_rows_w<2, SCALED>(aligned);
-    case 3: return pick_rows_w<3, SCALED>(aligned);
-    case 4: return pick_rows_w<4, SCALED>(aligned);
-    case 5: return pick_rows_w<5, SCALED>(aligned);
-    case 6: return pick_rows_w<6, SCALED>(aligned);
-    case 7: return pick_rows_w<7, SCALED>(aligned);
-    case 8: return pick_rows_w<8, SCALED>(aligned);
-    case 9: return pick_rows_w<9, SCALED>(aligned);
-    case 10: return pick_rows_w<10, SCALED>(aligned);
-    case 11: return pick_rows_w<11, SCALED>(aligned);
-    case 12: return pick_rows_w<12, SCALED>(aligned);
-    case 13: return pick_rows_w<13, SCALED>(aligned);
-    case 14: return pick_rows_w<14, SCALED>(aligned);
-    case 15: return pick_rows_w<15, SCALED>(aligned);
-    default: return pick_rows_w<16, SCALED>(aligned);
+    case 2: return k_fold_rows<2, SCALED>;
+    case 3: return k_fold_rows<3, SCALED>;
+    case 4: return k_fold_rows<4, SCALED>;
+    case 5: return k_fold_rows<5, SCALED>;
+    case 6: return k_fold_rows<6, SCALED>;
+    case 7: return k_fold_rows<7, SCALED>;
+    case 8: return k_fold_rows<8, SCALED>;
+    case 9: return k_fold_rows<9, SCALED>;
+    case 10: return k_fold_rows<10, SCALED>;
+    case 11: return k_fold_rows<11, SCALED>;
+    case 12: return k_fold_rows<12, SCALED>;
+    case 13: return k_fold_rows<13, SCALED>;
+    case 14: return k_fold_rows<14, SCALED>;
+    case 15: return k_fold_rows<15, SCALED>;
+    default: return k_fold_rows<16, SCALED>;
     }
 }
 
@@ -737,7 +837,7 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
     const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
     hipError_t e;
     if (p.path == DETFOLD_PATH_ROWS) {
-        rows_kernel_t k = scaled ? pick_rows<true>(w, vector_legal(g)) : pick_rows<false>(w, vector_legal(g));
+        rows_kernel_t k = scaled ? pick_rows<true>(w) : pick_rows<false>(w);
         SlotTable slots = {};
         for (int32_t r = 0; r < w; ++r)
             slots.p[r] = reinterpret_cast<const float *>(g.slot(r));
@@ -1046,6 +1146,131 @@ int run_pair(const detfold_pair_link *k, float *x0, float *x1, int64_t n)
     return DETFOLD_OK;
 }
 
+int check_link_events(const detfold_pair_link *k)
+{
+    return k && k->pushed[0] && k->pushed[1] && k->folded[0] && k->folded[1] ? DETFOLD_OK
+                                                                               : DETFOLD_EINVAL;
+}
+
+bool bad_buffer(const void *p, int64_t n)
+{
+    return !p || (((uintptr_t)p) & 3) || n > INT64_MAX / 8;
+}
+
+// Broadcast: stream[o] marks where it stands (folded[o]), stream[root] waits
+// for that mark, copies, and the copy's end (pushed[root]) gates stream[o].
+int run_broadcast(const detfold_pair_link *k, int32_t root, const float *src, float *dst, int64_t n)
+{
+    int32_t cu = 0;
+    int rc = current_cu_count(&cu);
+    if (rc != DETFOLD_OK)
+        return rc;
+    const int32_t o = 1 - root;
+    hipStream_t sr = static_cast<hipStream_t>(k->stream[root]);
+    hipStream_t so = static_cast<hipStream_t>(k->stream[o]);
+    if (hipEventRecord(static_cast<hipEvent_t>(k->folded[o]), so) != hipSuccess ||
+        hipStreamWaitEvent(sr, static_cast<hipEvent_t>(k->folded[o]), 0) != hipSuccess)
+        return DETFOLD_ELAUNCH;
+    if ((rc = copy_out(&dst, 1, src, n, cu, sr, static_cast<hipEvent_t>(k->pushed[root]))) != DETFOLD_OK)
+        return rc;
+    return hipStreamWaitEvent(so, static_cast<hipEvent_t>(k->pushed[root]), 0) == hipSuccess
+               ? DETFOLD_OK
+               : DETFOLD_ELAUNCH;
+}
+
+// All-gather: both streams mark where they stand; rank r, once the peer has
+// reached its mark, writes x_r into slot r of f_r and of f_peer in one copy
+// kernel; then each stream waits for the peer's copy.
+int run_all_gather(const detfold_pair_link *k, const float *x0, const float *x1, float *f0,
+                   float *f1, int64_t span)
+{
+    int32_t cu = 0;
+    int rc = current_cu_count(&cu);
+    if (rc != DETFOLD_OK)
+        return rc;
+    const float *x[2] = {x0, x1};
+    float *f[2] = {f0, f1};
+    hipStream_t st[2] = {static_cast<hipStream_t>(k->stream[0]), static_cast<hipStream_t>(k->stream[1])};
+    for (int r = 0; r < 2; ++r)
+        if (hipEventRecord(static_cast<hipEvent_t>(k->folded[r]), st[r]) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+    for (int r = 0; r < 2; ++r) {
+        if (hipStreamWaitEvent(st[r], static_cast<hipEvent_t>(k->folded[1 - r]), 0) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+        float *dsts[2] = {f[r] + (int64_t)r * span, f[1 - r] + (int64_t)r * span};
+        if ((rc = copy_out(dsts, 2, x[r], span, cu, st[r], static_cast<hipEvent_t>(k->pushed[r]))) != DETFOLD_OK)
+            return rc;
+    }
+    for (int r = 0; r < 2; ++r)
+        if (hipStreamWaitEvent(st[r], static_cast<hipEvent_t>(k->pushed[1 - r]), 0) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+    return DETFOLD_OK;
+}
+
+int check_one_shot_link(const detfold_one_shot_link *k)
+{
+    if (!k || !k->flags || !k->words || (((uintptr_t)k->flags) & 3) || (((uintptr_t)k->words) & 3) ||
+        k->spin_limit < 0 || k->capacity < 0)
+        return DETFOLD_EINVAL;
+    if (ranges_overlap((uintptr_t)k->flags, DETFOLD_ONE_SHOT_FLAG_WORDS * 4, (uintptr_t)k->words, 8))
+        return DETFOLD_EOVERLAP;
+    return DETFOLD_OK;
+}
+
+// The buffers one launch touches: the ranks' x (one or both) and both stages.
+int check_one_shot_buffers(const detfold_one_shot_link *k, const float *const *x, int nx, int64_t n)
+{
+    if (n < 0 || n > k->capacity)
+        return DETFOLD_EINVAL;
+    if (n == 0)
+        return DETFOLD_OK;
+    const float *p[4] = {k->stage[0], k->stage[1], x[0], nx > 1 ? x[1] : nullptr};
+    const int np = 2 + nx;
+    for (int i = 0; i < np; ++i) {
+        if (bad_buffer(p[i], n))
+            return DETFOLD_EINVAL;
+        for (int j = 0; j < i; ++j)
+            if (ranges_overlap((uintptr_t)p[i], (uint64_t)n * 4, (uintptr_t)p[j], (uint64_t)n * 4))
+                return DETFOLD_EOVERLAP;
+    }
+    return DETFOLD_OK;
+}
+
+// nranks = 2: both ranks in one launch (workgroups [0, G) rank 0, [G, 2G)
+// rank 1); nranks = 1: rank `rank0` alone.  G = ceil(n / 1024) capped at
+// DETFOLD_ONE_SHOT_BLOCKS; each workgroup takes a chunk rounded up to 4 floats.
+int run_one_shot(const detfold_one_shot_link *k, int32_t rank0, int nranks, float *xa, float *xb,
+                 int64_t n, hipStream_t stream)
+{
+    OneShotArgs a = {};
+    int64_t blocks = (n + kOneShotPerBlock - 1) / kOneShotPerBlock;
+    if (blocks > DETFOLD_ONE_SHOT_BLOCKS)
+        blocks = DETFOLD_ONE_SHOT_BLOCKS;
+    int64_t chunk = (n + blocks - 1) / blocks;
+    chunk = (chunk + 3) & ~(int64_t)3;
+    a.x[rank0] = xa;
+    if (nranks == 2)
+        a.x[1 - rank0] = xb;
+    a.stage[0] = k->stage[0];
+    a.stage[1] = k->stage[1];
+    a.flags = k->flags;
+    a.words = k->words;
+    a.n = n;
+    a.chunk = chunk;
+    a.blocks = (int32_t)blocks;
+    a.rank0 = rank0;
+    a.spin_limit = k->spin_limit ? k->spin_limit : kDefaultSpinLimit;
+    bool vec = true;
+    for (int r = 0; r < 2; ++r)
+        vec = vec && phase16((uintptr_t)a.stage[r]) == 0 && (!a.x[r] || phase16((uintptr_t)a.x[r]) == 0);
+    a.vec = vec;
+    void *args[] = {&a};
+    return hipLaunchKernel((const void *)k_one_shot, dim3((unsigned)(blocks * nranks)), dim3(kOneShotBlock),
+                           args, 0, stream) == hipSuccess
+               ? DETFOLD_OK
+               : DETFOLD_ELAUNCH;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1166,6 +1391,81 @@ int detfold_pair_all_reduce(const detfold_pair_link *link, float *x0, float *x1,
     if (rc != DETFOLD_OK || n == 0)
         return rc;
     return run_pair(link, x0, x1, n);
+}
+
+int detfold_pair_broadcast(const detfold_pair_link *link, int32_t root, const float *src,
+                           float *dst, int64_t n)
+{
+    if (check_link_events(link) != DETFOLD_OK || (root != 0 && root != 1) || n < 0)
+        return DETFOLD_EINVAL;
+    if (n == 0)
+        return DETFOLD_OK;
+    if (bad_buffer(src, n) || bad_buffer(dst, n))
+        return DETFOLD_EINVAL;
+    if (ranges_overlap((uintptr_t)src, (uint64_t)n * 4, (uintptr_t)dst, (uint64_t)n * 4))
+        return DETFOLD_EOVERLAP;
+    return run_broadcast(link, root, src, dst, n);
+}
+
+int detfold_pair_all_gather(const detfold_pair_link *link, const float *x0, const float *x1,
+                            float *f0, float *f1, int64_t span)
+{
+    if (check_link_events(link) != DETFOLD_OK || span < 0)
+        return DETFOLD_EINVAL;
+    if (span == 0)
+        return DETFOLD_OK;
+    if (bad_buffer(x0, span) || bad_buffer(x1, span) || bad_buffer(f0, 2 * span) || bad_buffer(f1, 2 * span))
+        return DETFOLD_EINVAL;
+    const uint64_t xb = (uint64_t)span * 4, fb = xb * 2;
+    if (ranges_overlap((uintptr_t)f0, fb, (uintptr_t)f1, fb) ||
+        ranges_overlap((uintptr_t)f0, fb, (uintptr_t)x0, xb) || ranges_overlap((uintptr_t)f0, fb, (uintptr_t)x1, xb) ||
+        ranges_overlap((uintptr_t)f1, fb, (uintptr_t)x0, xb) || ranges_overlap((uintptr_t)f1, fb, (uintptr_t)x1, xb))
+        return DETFOLD_EOVERLAP;
+    return run_all_gather(link, x0, x1, f0, f1, span);
+}
+
+int detfold_one_shot_init(const detfold_one_shot_link *link)
+{
+    int rc = check_one_shot_link(link);
+    if (rc != DETFOLD_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(link->stream);
+    uint32_t *flags = link->flags;
+    int64_t nf = DETFOLD_ONE_SHOT_FLAG_WORDS;
+    uint32_t *words = reinterpret_cast<uint32_t *>(link->words);
+    int64_t nw = 2;
+    void *a0[] = {&flags, &nf};
+    void *a1[] = {&words, &nw};
+    if (hipLaunchKernel((const void *)k_zero_words, dim3(1), dim3(kOneShotBlock), a0, 0, st) != hipSuccess ||
+        hipLaunchKernel((const void *)k_zero_words, dim3(1), dim3(kOneShotBlock), a1, 0, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return DETFOLD_ELAUNCH;
+    return DETFOLD_OK;
+}
+
+int detfold_one_shot_all_reduce(const detfold_one_shot_link *link, float *x0, float *x1, int64_t n)
+{
+    int rc = check_one_shot_link(link);
+    if (rc != DETFOLD_OK)
+        return rc;
+    float *x[2] = {x0, x1};
+    if ((rc = check_one_shot_buffers(link, x, 2, n)) != DETFOLD_OK || n == 0)
+        return rc;
+    return run_one_shot(link, 0, 2, x0, x1, n, static_cast<hipStream_t>(link->stream));
+}
+
+int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float *x, int64_t n,
+                          void *stream)
+{
+    int rc = check_one_shot_link(link);
+    if (rc != DETFOLD_OK)
+        return rc;
+    if (rank != 0 && rank != 1)
+        return DETFOLD_EINVAL;
+    float *xs[1] = {x};
+    if ((rc = check_one_shot_buffers(link, xs, 1, n)) != DETFOLD_OK || n == 0)
+        return rc;
+    return run_one_shot(link, rank, 1, x, nullptr, n, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -189,11 +189,104 @@ int detfold_pair_link_init(const detfold_pair_link *link);
  */
 int detfold_pair_all_reduce(const detfold_pair_link *link, float *x0, float *x1, int64_t n);
 
+/*
+ * detfold_pair_broadcast -- pure movement: the other rank's dst becomes a byte
+ * copy of rank `root`'s src (memra-engine tests/tp_ar_gpu.rs, the broadcast
+ * half of broadcast_and_all_gather_move_bytes_exactly).  The copy runs on
+ * stream[root] once stream[1-root] has reached this call (so earlier work
+ * there that reads dst is done); stream[1-root] then waits for the copy.
+ *   root    0 or 1
+ *   src     device pointer, n floats of rank root (read)
+ *   dst     device pointer, n floats of rank 1-root (overwritten)
+ * Errors: DETFOLD_EINVAL (NULL link or event, root not 0 or 1, n < 0, NULL or
+ * misaligned buffer), DETFOLD_EOVERLAP (src and dst intersect), DETFOLD_ELAUNCH.
+ * Uses the link's events (folded[], pushed[]) but not its staging buffers.
+ */
+int detfold_pair_broadcast(const detfold_pair_link *link, int32_t root, const float *src,
+                           float *dst, int64_t n);
+
+/*
+ * detfold_pair_all_gather -- pure movement: on both ranks f_r becomes the
+ * rank-order concatenation [x0 | x1] (2*span floats).  Rank r writes x_r into
+ * its own slot of f_r and into the same slot of the peer's f_{1-r} with one
+ * copy kernel on stream[r]; each stream then waits for the peer's copy.
+ *   x0, x1  device pointers, span floats each (read; they may alias each other)
+ *   f0, f1  device pointers, 2*span floats each (overwritten)
+ * Errors: DETFOLD_EINVAL, DETFOLD_EOVERLAP (f0, f1 and the x must not intersect),
+ * DETFOLD_ELAUNCH.
+ */
+int detfold_pair_all_gather(const detfold_pair_link *link, const float *x0, const float *x1,
+                            float *f0, float *f1, int64_t span);
+
+/*
+ * The one-shot arm of the two-rank all-reduce (memra-engine
+ * tests/tp_ar_gpu.rs, one_shot_all_reduce_matches_the_host_sum_bitwise; the
+ * module note there describes why a spinning fold can starve its peer on one
+ * device).  One kernel and no events: each workgroup b of rank r
+ *   1. copies its chunk of x_r into stage[1-r],
+ *   2. arrives at the entry barrier (counter flags[entry][r][b]) and waits
+ *      until the peer's workgroup b has arrived as often,
+ *   3. folds x_r[i] = x_r[i] + stage[r][i] over its chunk,
+ *   4. arrives at the exit barrier and waits for the peer's workgroup b (so
+ *      the next call's push cannot overwrite a stage the peer still reads).
+ * Every wait polls at most spin_limit times.  A wait that expires stores a
+ * barrier word and the workgroup returns: DETFOLD_BARRIER_ENTRY_EXPIRED
+ * (the fold was skipped, that chunk of x_r is untouched) or
+ * DETFOLD_BARRIER_EXIT_EXPIRED (the fold is done; the peer may still read
+ * the stage).  The first word stored for a rank stays until init.  After a
+ * nonzero word the counters disagree and the link must be re-initialised.
+ * The counters live on the device and are advanced by the kernel itself, so
+ * a call captured in a HIP graph replays correctly.
+ */
+#define DETFOLD_ONE_SHOT_BLOCKS 64 /* workgroups per rank, at most */
+#define DETFOLD_ONE_SHOT_FLAG_WORDS (2 * 2 * DETFOLD_ONE_SHOT_BLOCKS)
+#define DETFOLD_BARRIER_ENTRY_EXPIRED 40043
+#define DETFOLD_BARRIER_EXIT_EXPIRED 40044
+typedef struct detfold_one_shot_link {
+    void *stream;       /* hipStream_t for init and for detfold_one_shot_all_reduce */
+    float *stage[2];    /* stage[r]: rank r's staging buffer, capacity floats, device */
+    int64_t capacity;   /* floats each staging buffer holds */
+    uint32_t *flags;    /* device, DETFOLD_ONE_SHOT_FLAG_WORDS barrier counters */
+    int32_t *words;     /* device, 2 barrier words (rank 0, rank 1); 0 = no expiry */
+    int32_t spin_limit; /* polls per barrier wait before it expires; 0 = 1 << 20 */
+} detfold_one_shot_link;
+
+/* Zero flags and words with a kernel on link->stream and synchronize that
+ * stream.  Call once before the first all-reduce and after any nonzero word. */
+int detfold_one_shot_init(const detfold_one_shot_link *link);
+
+/*
+ * detfold_one_shot_all_reduce -- x0 = x0 + x1 and x1 = x1 + x0 (bit-identical),
+ * both ranks' workgroups in one launch on link->stream.  On one device that
+ * launch holds at most 2 * DETFOLD_ONE_SHOT_BLOCKS workgroups of 256 threads,
+ * all resident at once, so the barriers complete.
+ *   x0, x1  device pointers to n floats each (read and written)
+ *   n       0 <= n <= capacity
+ * Errors: DETFOLD_EINVAL (NULL link, flags, words or buffer, misaligned
+ * pointer, spin_limit < 0, n > capacity), DETFOLD_EOVERLAP (x0, x1, stage[0],
+ * stage[1] must be disjoint over n floats), DETFOLD_ELAUNCH.  An expired
+ * barrier is reported in link->words, not by the return code.
+ */
+int detfold_one_shot_all_reduce(const detfold_one_shot_link *link, float *x0, float *x1,
+                                int64_t n);
+
+/*
+ * detfold_one_shot_rank -- rank `rank`'s kernel alone, on `stream`: the shape
+ * each rank launches on its own device.  Both ranks must make the call with
+ * the same n.  On one device the two kernels must run concurrently for the
+ * barriers to meet; when they do not (both streams on one hardware queue, or
+ * the peer never launched), the waits expire and the words say so.
+ *   rank    0 or 1;  x  device pointer to n floats of that rank
+ * Errors: as detfold_one_shot_all_reduce, plus DETFOLD_EINVAL for a bad rank.
+ */
+int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float *x, int64_t n,
+                          void *stream);
+
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 4
+#define DETFOLD_ABI_VERSION 5
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------

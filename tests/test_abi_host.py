@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 4
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 5
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -152,7 +152,8 @@ def test_plan_w16_offset_arena(detfold_lib):
     with pytest.raises(detfold_lib.DetfoldError):
         detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU, dict(path=detfold_lib.PATH_VECTOR,
                                                                    block=0, grid=0, unroll=0, policy=0))
-    # ... but the LDS row body realigns them: 16-byte groups of out, 3 tail elements
+    # ... but the LDS row body loads each slot's tile from its own dword: 16-byte
+    # groups of out, 3 tail elements
     p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
     assert (p["head"], p["body"], p["tail"]) == (0, n // 4, 3)
@@ -181,7 +182,7 @@ def test_plan_head_and_tail(detfold_lib, phase_out, phase_in, n):
 
 def test_plan_ragged_length_with_several_slots(detfold_lib):
     # len % 4 != 0 puts slot 1 at another 16-byte phase than slot 0: the row
-    # body realigns it, the direct bodies fall back to 4-byte loads
+    # body takes it as it is, the direct bodies fall back to 4-byte loads
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 2, 1001, CU)
     assert p["path"] == detfold_lib.PATH_ROWS and (p["body"], p["tail"]) == (250, 1)
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 17, 1001, CU)
@@ -333,3 +334,68 @@ def test_pair_all_reduce_rejects_bad_arguments(detfold_lib):
     assert lib.detfold_pair_all_reduce(ctypes.byref(link), BASE + 8, x1, 16) == EOVERLAP  # x0 vs stage 0
     assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0 + 2, x1, 16) == EINVAL  # misaligned
     assert lib.detfold_pair_all_reduce(ctypes.byref(link), x0, x1, 0) == OK           # nothing to do
+
+
+def test_pair_broadcast_and_all_gather_reject_bad_arguments(detfold_lib):
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.OK
+    link = detfold_lib.PairLinkC()
+    src, dst = BASE, BASE + (1 << 20)
+    assert lib.detfold_pair_broadcast(None, 0, src, dst, 16) == EINVAL
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 0, src, dst, 16) == EINVAL   # no events
+    for i in range(2):  # fake event handles: never passed to HIP by the checks below
+        link.pushed[i], link.folded[i] = 0x1000 + i, 0x2000 + i
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 2, src, dst, 16) == EINVAL   # no rank 2
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), -1, src, dst, 16) == EINVAL
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 0, src, dst, -1) == EINVAL
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 0, None, dst, 16) == EINVAL
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 1, src, dst + 1, 16) == EINVAL  # misaligned
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 1, src, src + 60, 16) == EOVERLAP
+    assert lib.detfold_pair_broadcast(ctypes.byref(link), 0, src, dst, 0) == OK        # nothing to do
+    x0, x1, f0, f1 = BASE, BASE + (1 << 20), BASE + (2 << 20), BASE + (3 << 20)
+    assert lib.detfold_pair_all_gather(None, x0, x1, f0, f1, 16) == EINVAL
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), x0, x1, f0, f1, -1) == EINVAL
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), x0, None, f0, f1, 16) == EINVAL
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), x0, x1, f0 + 2, f1, 16) == EINVAL
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), x0, x1, f0, f0 + 64, 16) == EOVERLAP  # f0 is 128 B
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), x0, f1 + 100, f0, f1, 16) == EOVERLAP
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), f0 + 64, x1, f0, f1, 16) == EOVERLAP
+    assert lib.detfold_pair_all_gather(ctypes.byref(link), x0, x1, f0, f1, 0) == OK
+
+
+def test_one_shot_rejects_bad_arguments(detfold_lib):
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.OK
+    assert detfold_lib.ONE_SHOT_FLAG_WORDS == 256
+    link = detfold_lib.OneShotLinkC()
+    link.capacity = 4096
+    link.stage[0], link.stage[1] = BASE, BASE + (1 << 20)
+    x0, x1 = BASE + (2 << 20), BASE + (3 << 20)
+    ar = lib.detfold_one_shot_all_reduce
+    assert ar(None, x0, x1, 16) == EINVAL
+    assert ar(ctypes.byref(link), x0, x1, 16) == EINVAL                  # no flags or words
+    assert lib.detfold_one_shot_init(ctypes.byref(link)) == EINVAL
+    link.flags, link.words = BASE + (4 << 20), BASE + (5 << 20)
+    link.spin_limit = -1
+    assert ar(ctypes.byref(link), x0, x1, 16) == EINVAL                  # negative spin limit
+    assert lib.detfold_one_shot_init(ctypes.byref(link)) == EINVAL
+    link.spin_limit = 0
+    link.words = link.flags + 4 * 255                                     # words inside the counters
+    assert ar(ctypes.byref(link), x0, x1, 16) == EOVERLAP
+    assert lib.detfold_one_shot_init(ctypes.byref(link)) == EOVERLAP
+    link.words = link.flags + 4 * 256                                     # right after them: fine
+    link.flags += 2
+    assert ar(ctypes.byref(link), x0, x1, 16) == EINVAL                  # misaligned counters
+    link.flags -= 2
+    assert ar(ctypes.byref(link), x0, x1, 4097) == EINVAL                # over capacity
+    assert ar(ctypes.byref(link), x0, x1, -1) == EINVAL
+    assert ar(ctypes.byref(link), x0, x0 + 4, 16) == EOVERLAP
+    assert ar(ctypes.byref(link), BASE + 8, x1, 16) == EOVERLAP          # x0 vs stage 0
+    assert ar(ctypes.byref(link), x0 + 1, x1, 16) == EINVAL              # misaligned
+    assert ar(ctypes.byref(link), x0, x1, 0) == OK                       # nothing to do
+    rk = lib.detfold_one_shot_rank
+    assert rk(ctypes.byref(link), 2, x0, 16, None) == EINVAL
+    assert rk(ctypes.byref(link), -1, x0, 16, None) == EINVAL
+    assert rk(ctypes.byref(link), 1, BASE + (1 << 20) + 32, 16, None) == EOVERLAP  # x vs stage 1
+    assert rk(ctypes.byref(link), 0, x0, 4097, None) == EINVAL
+    assert rk(ctypes.byref(link), 0, x0, 0, None) == OK

@@ -235,7 +235,7 @@ def test_w16_offset_arena_shards_equal_whole(env):
     assert stacked.data_ptr() % 16 == 4
     stacked.copy_(torch.from_numpy(host))
     out_w = torch.empty(n, dtype=torch.float32, device=dev)
-    df.fold_ranks(out_w, stacked)  # the LDS row body, realigning the shifted slots
+    df.fold_ranks(out_w, stacked)  # the LDS row body, slots at three phases other than out's
     whole = _host(out_w)
     _assert_bits(whole, want, "W=16 whole arena")
     out_w.fill_(float("nan"))
