@@ -284,6 +284,7 @@ def bench_join(args, torch, df, dev, timer):
         graph.replay()
         torch.cuda.synchronize()
         in_graph = timer.region(graph.replay, 10) / (10 * k_graph)
+        del graph
         row = {"n": n, "bytes_per_call": 12 * n,
                "python_back_to_back_us_per_call": round(b2b * 1e3, 3),
                "graph_replay_us_per_call": round(in_graph * 1e3, 3)}
@@ -298,12 +299,35 @@ def bench_join(args, torch, df, dev, timer):
         sweep.append(row)
         log("fold_into n=%6d: %.3f us/call via python, %.3f us/call in a graph"
             % (n, b2b * 1e3, in_graph * 1e3))
-        del graph
     at16 = dict(next(r for r in sweep if r["n"] == 4096))
     at16["sweep"] = sweep
+    at16["launch_floor_graph_us_per_call"] = round(launch_floor(torch, dev, timer, k_graph) * 1e3, 3)
+    log("launch floor (a 1-element fill kernel, same graph method): %.3f us/call"
+        % at16["launch_floor_graph_us_per_call"])
     at16["note"] = ("graph_replay_us_per_call: device time per in-place fold, 200 calls captured "
                     "in one HIP graph; python_back_to_back is bounded by host launch cost")
     return at16
+
+
+def launch_floor(torch, dev, timer, k_graph) -> float:
+    """ms per launch of a minimal kernel (torch's fill of one element), captured
+    and replayed exactly as the fold_into calls are: the floor under them."""
+    x = torch.zeros(1, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            x.fill_(1.0)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(k_graph):
+            x.fill_(1.0)
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = timer.region(graph.replay, 10) / (10 * k_graph)
+    del graph
+    return ms
 
 
 def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
@@ -318,7 +342,7 @@ def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
     want = fn()
     times = []
     t_start = time.perf_counter()
-    while (time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3) and len(times) < 200:
+    while (time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3) and len(times) < 5000:
         t0 = time.perf_counter()
         fn()
         times.append(time.perf_counter() - t0)

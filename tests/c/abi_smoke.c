@@ -26,5 +26,22 @@ int main(void)
     rc = detfold_plan_fold_ranks(base, base + (1u << 30), 8, (int64_t)1 << 24, 256, &launch, &plan);
     printf("plan %d %d %d %lld %lld\n", rc, plan.path, plan.block, (long long)plan.grid,
            (long long)plan.tile);
+
+    /* the two-rank links from C: struct layout and the checks made before any HIP call */
+    detfold_one_shot_link shot = {0};
+    shot.capacity = 1024;
+    shot.stage[0] = (float *)(base + (2u << 20));
+    shot.stage[1] = (float *)(base + (3u << 20));
+    printf("shot_noflags %d\n", detfold_one_shot_all_reduce(&shot, out, out + 4096, 16));
+    shot.flags = (uint32_t *)(base + (4u << 20));
+    shot.words = (int32_t *)(base + (5u << 20));
+    printf("shot_capacity %d\n", detfold_one_shot_all_reduce(&shot, out, out + 4096, 1025));
+    printf("shot_rank %d\n", detfold_one_shot_rank(&shot, 2, out, 16, NULL));
+    printf("shot_empty %d\n", detfold_one_shot_all_reduce(&shot, out, out + 4096, 0));
+    printf("shot_words %d %d %d\n", DETFOLD_ONE_SHOT_FLAG_WORDS, DETFOLD_BARRIER_ENTRY_EXPIRED,
+           DETFOLD_BARRIER_EXIT_EXPIRED);
+    detfold_pair_link pair = {{NULL, NULL}, {NULL, NULL}, 0, {NULL, NULL}, {NULL, NULL}};
+    printf("bcast_noevents %d\n", detfold_pair_broadcast(&pair, 0, stacked, out, 16));
+    printf("gather_noevents %d\n", detfold_pair_all_gather(&pair, stacked, stacked, out, out + 64, 16));
     return 0;
 }

@@ -28,3 +28,10 @@ def test_c99_caller(tmp_path, detfold_lib):
     assert "overlap" in lines["strerror"]
     assert lines["shards"] == "0 4 3 3"
     assert lines["plan"] == "0 %d 512 32768 128" % detfold_lib.PATH_ROWS
+    assert lines["shot_noflags"] == str(detfold_lib.EINVAL)
+    assert lines["shot_capacity"] == str(detfold_lib.EINVAL)
+    assert lines["shot_rank"] == str(detfold_lib.EINVAL)
+    assert lines["shot_empty"] == str(detfold_lib.OK)
+    assert lines["shot_words"] == "256 40043 40044"
+    assert lines["bcast_noevents"] == str(detfold_lib.EINVAL)
+    assert lines["gather_noevents"] == str(detfold_lib.EINVAL)
