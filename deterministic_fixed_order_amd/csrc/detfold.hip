@@ -571,7 +571,7 @@ int check_override(const detfold_launch *o)
 
 // Path and geometry for one call.
 //  * Streaming policy, 2 <= W <= 16: the LDS row body, one wave per slot
-//    (block = 64*W), one tile of 64*(64/W clamped to 2..16) groups per
+//    (block = 64*W), a tile of 64 * rows_kib_per_wave(W) groups per
 //    workgroup, one pass.
 //  * Otherwise the direct bodies: vector when `out` and every slot share a
 //    16-byte phase, else scalar; kStreamBlock threads, halved (down to 64)

@@ -19,11 +19,13 @@
  *     current HIP device; `stream` is a hipStream_t of that device passed as
  *     void* (NULL = the null stream).
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
- *     pointer after it returns, and does not synchronize: work is enqueued on
- *     `stream` and the call returns.  Faults inside the kernels surface at the
- *     caller's next synchronization of that stream.
+ *     pointer after it returns, and does not synchronize (detfold_one_shot_init
+ *     excepted): work is enqueued on `stream` and the call returns.  Faults
+ *     inside the kernels surface at the caller's next synchronization of that
+ *     stream.
  *   - Float pointers must be 4-byte aligned; any 4-byte alignment is accepted
- *     (misaligned or ragged lengths take a scalar path, never an error).
+ *     (buffers at different offsets modulo 16 bytes and ragged lengths are
+ *     handled by dword-addressed or 4-byte loads, never an error).
  *   - A call with zero elements returns DETFOLD_OK and launches nothing
  *     (mamba-rs src/dist/reducer.rs, `DetReduceKernel::launch`).
  *   - Every entry point validates its arguments before any HIP call, so an
@@ -311,8 +313,9 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
  * and the cache policy never change a bit:
  *   ROWS    (default for 2 <= W <= 16 on the streaming policy) one workgroup of
  *           W waves per tile; wave r streams a contiguous run of slot r into
- *           LDS with 16-byte loads, realigning slots whose 16-byte phase
- *           differs from out's; every thread then folds whole 16-byte groups
+ *           LDS with 16-byte loads addressed from the slot's own first element
+ *           of the tile, so a slot at another 16-byte phase than out's lands
+ *           aligned all the same; every thread then folds whole 16-byte groups
  *           and stores them.  Up to 3 elements before the first 16-byte
  *           boundary of `out` (head) and up to 3 after the last (tail) are
  *           folded one by one.
