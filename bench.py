@@ -43,11 +43,13 @@ WORKLOADS = {
     "w8": ("vecf", 8, 1 << 24, 1000, None, 0),
     "w4": ("mixed", 4, 100_000_000, 2000, 0.25, 0),
     "w16": ("vecf", 16, 10_000_019, 3000, None, 1),
+    "w32": ("vecf", 32, 8_000_001, 4000, None, 1),
 }
 WORKLOAD_NAMES = {
     "w8": "fold_ranks W=8 stacked [8][16777216] f32 (64 MiB/slot), uniform [-1,1)",
     "w4": "fold_ranks_scaled W=4 stacked [4][100000000] f32, mixed magnitudes, inv_w=0.25",
     "w16": "fold_ranks W=16 stacked [16][10000019] f32 at base+1 element, uniform [-1,1)",
+    "w32": "fold_ranks W=32 stacked [32][8000001] f32 at base+1 element, uniform [-1,1)",
     "join": "fold_into n=4096 f32 (16 KiB per buffer)",
     "round": "loopback_round W=8 arenas of 16777216 f32 (64 MiB each), staged and direct",
     "pair": "two-stream pair all-reduce at the decode-join sizes",
@@ -238,6 +240,9 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     """Name of the kernel instance the default launch uses (from the host plan)."""
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
     p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
+    if p["path"] == df.PATH_ROWS and W > 16:
+        return "k_fold_rows_wide<%s> grid=%d block=%d tile=%d" % (
+            str(scaled).lower(), p["grid"], p["block"], p["tile"])
     if p["path"] == df.PATH_ROWS:
         return "k_fold_rows<%d,%s> grid=%d block=%d tile=%d" % (
             W, str(scaled).lower(), p["grid"], p["block"], p["tile"])

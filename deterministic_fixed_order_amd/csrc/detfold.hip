@@ -17,7 +17,7 @@
 //    add, so the adds wait on data, not the reverse.  `unroll` groups per thread
 //    per pass multiply the bytes in flight.
 //  * When `out` and the slots sit at different offsets modulo 16 bytes no
-//    element index lines them all up.  The LDS row body (2 <= W <= 16) still
+//    element index lines them all up.  The LDS row bodies (W >= 2) still
 //    moves 16-byte blocks: each wave's buffer descriptor starts at its own
 //    slot's first element of the tile.  The direct bodies give each lane one
 //    4-byte element per slot instead (a wave still reads 256 contiguous bytes
@@ -51,6 +51,8 @@ constexpr int kMaxBlock = 1024;
 constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth path
 constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
 constexpr int kMaxRowsW = 16;      // widest fold the LDS row body takes (one wave per slot)
+constexpr int kWideWaves = 16;     // slots per pass of the wide row body (W > kMaxRowsW)
+constexpr int kWideKiB = 4;        // KiB of one slot each wave of the wide body streams per pass
 
 // KiB of one slot each wave of the LDS row body streams per tile: ceil(W/4)
 // for W >= 3, 8 for W = 2.  Measured on MI355X over W = 2..16 and 1/2/4/8 KiB
@@ -341,6 +343,79 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slot
     }
 }
 
+// Wide LDS row body (W > 16, stacked arena): a workgroup of 16 waves folds a
+// tile of 256 groups in passes of 16 slots.  In pass p wave q streams 4 KiB of
+// slot 16p + q into LDS row q, exactly as the row body above does; after the
+// barrier the thread that owns group t continues its chain with rows 0, 1, ...
+// of the pass -- pass 0 starts it from slot 0 -- and a second barrier frees
+// the rows for the next pass.  The running sum stays in the thread's
+// registers between passes, so each element still sees the adds in strictly
+// ascending slot order, one rounding each, and is stored once at the end.
+template <bool SCALED>
+__global__ __launch_bounds__(kWideWaves * 64) void k_fold_rows_wide(float *out, const float *s0,
+                                                                    const float *s1, int64_t stride,
+                                                                    int w, int64_t len, int64_t head,
+                                                                    float inv_w)
+{
+    constexpr int T = kWideKiB * 64;  // groups per tile, at most one per thread
+    static_assert(T <= kWideWaves * 64, "one group per thread");
+    __shared__ f4 rows[kWideWaves][T];
+
+    const int64_t groups = (len - head) >> 2;
+    const int64_t tail0 = head + (groups << 2);
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < head + (len - tail0))
+        fold_one<0, SCALED>(out, s0, s1, stride, w, gid < head ? gid : tail0 + (gid - head), inv_w);
+
+    const uint32_t lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint32_t t = threadIdx.x;
+    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
+        const int64_t g0 = tile * T;
+        const int64_t cnt = groups - g0 < T ? groups - g0 : T;
+        const int64_t e0 = head + 4 * g0;
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int base = 0; base < w; base += kWideWaves) {
+            const int nr = w - base < kWideWaves ? w - base : kWideWaves;
+            if (wave < nr) {
+                const int r = base + wave;
+                const float *slot = r == 0 ? s0 : s1 + (int64_t)(r - 1) * stride;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot + e0, (uint32_t)(cnt * 16));
+#pragma unroll
+                for (int u = 0; u < kWideKiB; ++u)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[wave][u * 64], 16,
+                                                             (uint32_t)(u * 64 + lane) * 16u, 0, 0,
+                                                             Aux<kStream>::load);
+            }
+            __syncthreads();  // this pass's rows have landed
+            if (t < (uint32_t)cnt) {
+                int q = 0;
+                if (base == 0) {
+                    acc = rows[0][t];  // the chain starts from slot 0 itself
+                    q = 1;
+                }
+                // rows are read four at a time so the LDS reads overlap; the
+                // adds still take slot base + q in ascending order
+                for (; q + 4 <= nr; q += 4) {
+                    const f4 a0 = rows[q][t], a1 = rows[q + 1][t], a2 = rows[q + 2][t], a3 = rows[q + 3][t];
+                    acc = acc + a0;
+                    acc = acc + a1;
+                    acc = acc + a2;
+                    acc = acc + a3;
+                }
+                for (; q < nr; ++q)
+                    acc = acc + rows[q][t];
+            }
+            __syncthreads();  // every thread has read the rows before they are refilled
+        }
+        if (t < (uint32_t)cnt) {
+            if constexpr (SCALED)
+                acc = acc * inv_w;  // one rounding of the finished sum
+            bstore<Aux<kStream>::store>(acc, make_rsrc(out + e0, (uint32_t)(cnt * 16)), t * 16u);
+        }
+    }
+}
+
 // Byte movement for the one-device rounds: copy `n` floats from `src` into
 // every one of `ndst` destinations (src read once).  VEC: src and every
 // destination share one 16-byte phase -- 16-byte groups after `head` scalar
@@ -544,6 +619,11 @@ bool vector_legal(const Geometry &g)
     return true;
 }
 
+// Workgroup size and tile (16-byte groups) of the row bodies: one wave per
+// slot up to 16 slots, 16 waves making passes over the slots beyond that.
+int rows_block(int32_t w) { return w <= kMaxRowsW ? 64 * w : 64 * kWideWaves; }
+int64_t rows_tile(int32_t w) { return (int64_t)(w <= kMaxRowsW ? rows_kib_per_wave(w) : kWideKiB) * 64; }
+
 // Positions per thread per pass.  The vector body moves 16 bytes per slot per
 // position, and one position per thread keeps the most waves in flight (the
 // measured best on MI355X); the scalar body moves 4 bytes per slot per
@@ -570,9 +650,10 @@ int check_override(const detfold_launch *o)
 }
 
 // Path and geometry for one call.
-//  * Streaming policy, 2 <= W <= 16: the LDS row body, one wave per slot
+//  * Streaming policy, W >= 2: the LDS row body, one wave per slot
 //    (block = 64*W), a tile of 64 * rows_kib_per_wave(W) groups per
-//    workgroup, one pass.
+//    workgroup, one pass; beyond 16 slots (stacked arenas) the wide row body,
+//    16 waves making passes of 16 slots over tiles of 256 groups.
 //  * Otherwise the direct bodies: vector when `out` and every slot share a
 //    16-byte phase, else scalar; kStreamBlock threads, halved (down to 64)
 //    while that would leave compute units without a workgroup; one pass.
@@ -591,7 +672,7 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
         policy = o.policy;
 
     const bool vec_ok = vector_legal(g);
-    const bool rows_ok = g.w >= 2 && g.w <= kMaxRowsW;
+    const bool rows_ok = g.w >= 2 && (g.w <= kMaxRowsW || !g.has_table);
     if (g.has_table && g.w >= 2 && (o.path == DETFOLD_PATH_VECTOR || o.path == DETFOLD_PATH_SCALAR ||
                                     policy == DETFOLD_POLICY_CACHED))
         return DETFOLD_EINVAL;  // separate slot buffers have only the LDS row body
@@ -605,7 +686,8 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
     if (path == DETFOLD_PATH_VECTOR && !vec_ok)
         return DETFOLD_EINVAL;
     if (path == DETFOLD_PATH_ROWS &&
-        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && o.block != 64 * g.w) || o.unroll > 1))
+        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && o.block != rows_block(g.w)) ||
+         o.unroll > 1))
         return DETFOLD_EINVAL;
 
     p->path = path;
@@ -624,8 +706,8 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
     }
     if (path == DETFOLD_PATH_ROWS) {
         p->unroll = 1;
-        p->block = 64 * g.w;
-        p->tile = (int64_t)rows_kib_per_wave(g.w) * 64;
+        p->block = rows_block(g.w);
+        p->tile = rows_tile(g.w);
     } else {
         p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
         int block = o.block;
@@ -836,7 +918,11 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
     const int policy = p.policy == DETFOLD_POLICY_CACHED ? kCached : kStream;
     const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
     hipError_t e;
-    if (p.path == DETFOLD_PATH_ROWS) {
+    if (p.path == DETFOLD_PATH_ROWS && w > kMaxRowsW) {
+        const void *k = scaled ? (const void *)k_fold_rows_wide<true> : (const void *)k_fold_rows_wide<false>;
+        void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
+        e = launch(k, grid, block, args, stream, done);
+    } else if (p.path == DETFOLD_PATH_ROWS) {
         rows_kernel_t k = scaled ? pick_rows<true>(w) : pick_rows<false>(w);
         SlotTable slots = {};
         for (int32_t r = 0; r < w; ++r)

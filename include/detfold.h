@@ -311,17 +311,19 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
  *
  * Three bodies compute the same per-element chain, so the path, the geometry
  * and the cache policy never change a bit:
- *   ROWS    (default for 2 <= W <= 16 on the streaming policy) one workgroup of
- *           W waves per tile; wave r streams a contiguous run of slot r into
+ *   ROWS    (default for W >= 2 on the streaming policy) one workgroup of
+ *           W waves per tile (beyond 16 slots: 16 waves making passes of 16
+ *           slots, the running sums kept in registers between passes); wave r
+ *           streams a contiguous run of slot r into
  *           LDS with 16-byte loads addressed from the slot's own first element
  *           of the tile, so a slot at another 16-byte phase than out's lands
  *           aligned all the same; every thread then folds whole 16-byte groups
  *           and stores them.  Up to 3 elements before the first 16-byte
  *           boundary of `out` (head) and up to 3 after the last (tail) are
  *           folded one by one.
- *   VECTOR  (default for W = 1 or W > 16 when `out` and every slot share one
- *           16-byte phase, and for the small in-place fold) each thread loads
- *           16 bytes of every slot directly; head and tail as above.
+ *   VECTOR  (default for W = 1 when `out` and slot 0 share one 16-byte phase,
+ *           and for the small in-place fold) each thread loads 16 bytes of
+ *           every slot directly; head and tail as above.
  *   SCALAR  (otherwise) each thread loads 4 bytes of every slot directly.
  *
  * Cache policy: the bandwidth path (fold_ranks, fold_ranks_scaled, and
@@ -332,7 +334,7 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
 #define DETFOLD_PATH_AUTO 0
 #define DETFOLD_PATH_VECTOR 1 /* direct body, 16-byte loads (out and every slot co-aligned) */
 #define DETFOLD_PATH_SCALAR 2 /* direct body, 4-byte loads (any alignment)                 */
-#define DETFOLD_PATH_ROWS 3   /* LDS row body, 2 <= W <= 16, any alignment, streaming only  */
+#define DETFOLD_PATH_ROWS 3   /* LDS row body, W >= 2, any alignment, streaming only        */
 
 #define DETFOLD_POLICY_DEFAULT 0
 #define DETFOLD_POLICY_STREAM 1 /* non-temporal loads, write-through stores */

@@ -130,7 +130,9 @@ def test_plan_rows_tile_per_width(detfold_lib, W, kib):
 @pytest.mark.parametrize("n,block", [(1 << 20, 512), (1 << 19, 512), (1 << 18, 256), (1 << 16, 64),
                                      (4096, 64), (4, 64)])
 def test_plan_direct_block_shrinks_to_cover_the_chip(detfold_lib, W, n, block):
-    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, n, CU)
+    # W = 1 takes the direct vector body by default; wider folds only when asked
+    launch = None if W == 1 else dict(path=detfold_lib.PATH_VECTOR, block=0, grid=0, unroll=0, policy=0)
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, n, CU, launch)
     assert p["path"] == detfold_lib.PATH_VECTOR
     assert p["block"] == block and p["tile"] == block
     assert p["grid"] == max(1, -(-p["body"] // block))
@@ -186,7 +188,11 @@ def test_plan_ragged_length_with_several_slots(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 2, 1001, CU)
     assert p["path"] == detfold_lib.PATH_ROWS and (p["body"], p["tail"]) == (250, 1)
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 17, 1001, CU)
-    assert p["path"] == detfold_lib.PATH_SCALAR
+    assert p["path"] == detfold_lib.PATH_ROWS and (p["body"], p["tail"]) == (250, 1)
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 17, 1001, CU,
+                                    dict(path=detfold_lib.PATH_AUTO, block=0, grid=0, unroll=0,
+                                         policy=detfold_lib.POLICY_CACHED))
+    assert p["path"] == detfold_lib.PATH_SCALAR  # the unhinted direct body, 4-byte loads
     # one slot: only out and slot 0 matter
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 1, 1001, CU)
     assert p["path"] == detfold_lib.PATH_VECTOR and p["tail"] == 1
@@ -211,7 +217,8 @@ def test_plan_override(detfold_lib):
 
 
 @pytest.mark.parametrize("W,launch", [(8, dict(block=256)), (8, dict(unroll=2)),
-                                      (8, dict(policy=2)), (1, {}), (17, {})])
+                                      (8, dict(policy=2)), (1, {}), (17, dict(block=512)),
+                                      (24, dict(unroll=2))])
 def test_plan_rejects_impossible_row_overrides(detfold_lib, W, launch):
     cfg = dict(path=detfold_lib.PATH_ROWS, block=0, grid=0, unroll=0, policy=0)
     cfg.update(launch)
@@ -399,3 +406,18 @@ def test_one_shot_rejects_bad_arguments(detfold_lib):
     assert rk(ctypes.byref(link), 1, BASE + (1 << 20) + 32, 16, None) == EOVERLAP  # x vs stage 1
     assert rk(ctypes.byref(link), 0, x0, 4097, None) == EINVAL
     assert rk(ctypes.byref(link), 0, x0, 0, None) == OK
+
+
+@pytest.mark.parametrize("W", [17, 24, 32, 33, 64, 100])
+@pytest.mark.parametrize("n", [1 << 22, 10_000_019, 4099])
+def test_plan_wide_rows(detfold_lib, W, n):
+    # beyond 16 slots: 16 waves making passes of 16 slots over 256-group tiles
+    for out, stacked in ((BASE, BASE + (1 << 36)), (BASE + 4, BASE + (1 << 36) + 12)):
+        p = detfold_lib.plan_fold_ranks(out, stacked, W, n, CU)
+        assert p["path"] == detfold_lib.PATH_ROWS
+        assert (p["block"], p["tile"], p["unroll"]) == (1024, 256, 1)
+        assert p["grid"] == max(1, -(-p["body"] // 256))
+        assert p["head"] + 4 * p["body"] + p["tail"] == n
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 36), W, n, CU,
+                                    dict(path=detfold_lib.PATH_ROWS, block=1024, grid=3, unroll=0, policy=0))
+    assert (p["block"], p["grid"]) == (1024, 3)

@@ -270,7 +270,7 @@ GEOMS = [dict(path=p, block=b, grid=g, unroll=u, policy=pol)
 ROW_GEOMS = [dict(path=3, block=b, grid=g, unroll=0, policy=0) for b in (0, -1) for g in (0, 1, 7)]
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 9, 16, 17, 24])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 9, 16, 17, 24, 33, 64])
 def test_geometry_independence(env, W):
     df, torch, dev = env
     n = 3 * (1 << 15) + 4  # several tiles; a multiple of 4 so the vector body is legal
@@ -280,8 +280,9 @@ def test_geometry_independence(env, W):
     stacked = _to_dev(torch, dev, host)
     out = torch.empty(n, dtype=torch.float32, device=dev)
     geoms = list(GEOMS)
-    if 2 <= W <= 16:  # the LDS row body; block -1 stands for its own size, 64*W
-        geoms += [dict(g, block=64 * W if g["block"] < 0 else 0) for g in ROW_GEOMS]
+    if W >= 2:  # the LDS row bodies; block -1 stands for their own size, 64*W or 1024 beyond 16
+        rb = 64 * W if W <= 16 else 1024
+        geoms += [dict(g, block=rb if g["block"] < 0 else 0) for g in ROW_GEOMS]
     for geom in geoms:
         if W >= 16 and geom["unroll"] == 4 and geom["block"] == 1024:
             continue  # legal but spills registers; covered at smaller blocks
@@ -295,7 +296,7 @@ def test_geometry_independence(env, W):
 
 @pytest.mark.parametrize("out_off,in_off", [(0, 0), (1, 1), (2, 2), (3, 3), (0, 1), (3, 0), (2, 1)])
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 4099, 4100, 65536 + 3])
-@pytest.mark.parametrize("W", [1, 2, 4, 7])
+@pytest.mark.parametrize("W", [1, 2, 4, 7, 19])
 def test_alignment_phases_and_ragged_lengths(env, out_off, in_off, n, W):
     df, torch, dev = env
     host = fold_inputs.slots("mixed", W, n, 7 * n + W)
@@ -506,3 +507,29 @@ def test_lengths_beyond_int32(env):
     del out
     df.fold_into(stacked[0], stacked[1])  # in place, streaming path
     _assert_bits(_host(stacked[0][idx_dev]), want, "fold_into at 2^31+13")
+
+
+@pytest.mark.parametrize("W,n,off", [(32, 1 << 23, 0), (33, 3_000_001, 1), (64, 1 << 20, 2), (17, 7_000_003, 3)])
+def test_wide_arena_rows_equal_direct_and_oracle(env, W, n, off):
+    # beyond 16 slots the wide row body folds in passes of 16 slots; its bits
+    # must equal the oracle's and both direct bodies'
+    df, torch, dev = env
+    host = fold_inputs.slots("varied", W, n, 7000 + W, spread=2.0)
+    want = oracle.fold_stacked(host)
+    want_s = oracle.fold_stacked_scaled(host, np.float32(1.0 / W))
+    alloc = torch.empty(W * n + 4, dtype=torch.float32, device=dev)
+    stacked = alloc[off:off + W * n].view(W, n)
+    stacked.copy_(torch.from_numpy(host))
+    del host
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    _say("case: wide arena W=%d n=%d off=%d rows" % (W, n, off))
+    df.fold_ranks(out, stacked)
+    _assert_bits(_host(out), want, "W=%d rows" % W)
+    df.fold_ranks_scaled(out, stacked, 1.0 / W)
+    _assert_bits(_host(out), want_s, "W=%d rows scaled" % W)
+    paths = [2] + ([1] if off == 0 and n % 4 == 0 else [])
+    for path in paths:
+        _say("case: wide arena W=%d n=%d off=%d path %d" % (W, n, off, path))
+        out.fill_(float("nan"))
+        df.fold_ranks_ex(out, stacked, path=path)
+        _assert_bits(_host(out), want, "W=%d path %d" % (W, path))
