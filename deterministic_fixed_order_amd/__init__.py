@@ -332,14 +332,30 @@ class OneShotLink:
     ``barrier_words()`` reads the two words: 0, or ``BARRIER_ENTRY_EXPIRED`` /
     ``BARRIER_EXIT_EXPIRED`` when a wait ran out of polls."""
 
-    def __init__(self, capacity: int, device=None, stream=None, spin_limit: int = 0):
+    def __init__(self, capacity: int, device=None, stream=None, spin_limit: int = 0,
+                 buffers=None, init: bool = True):
+        """``buffers``: an existing link's ``(stage, flags, words)`` -- for
+        instance tensors shared from another process -- used in place of new
+        ones; ``init=False`` then leaves their counters as they are."""
         import torch
         dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.device = dev
         self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
-        self.stage = [torch.empty(max(capacity, 1), dtype=torch.float32, device=dev) for _ in range(2)]
-        self.flags = torch.empty(ONE_SHOT_FLAG_WORDS, dtype=torch.int32, device=dev)
-        self.words = torch.empty(2, dtype=torch.int32, device=dev)
+        if buffers is None:
+            self.stage = [torch.empty(max(capacity, 1), dtype=torch.float32, device=dev) for _ in range(2)]
+            self.flags = torch.empty(ONE_SHOT_FLAG_WORDS, dtype=torch.int32, device=dev)
+            self.words = torch.empty(2, dtype=torch.int32, device=dev)
+        else:
+            stage, self.flags, self.words = buffers
+            self.stage = list(stage)
+            for t in self.stage:
+                _f32_device(t, "stage")
+                if t.numel() < capacity:
+                    raise ValueError("stage holds %d floats, capacity is %d" % (t.numel(), capacity))
+            if self.flags.dtype != torch.int32 or self.flags.numel() < ONE_SHOT_FLAG_WORDS:
+                raise ValueError("flags must be int32 with %d words" % ONE_SHOT_FLAG_WORDS)
+            if self.words.dtype != torch.int32 or self.words.numel() < 2:
+                raise ValueError("words must be int32 with 2 words")
         self.capacity = capacity
         self._c = OneShotLinkC()
         self._c.stream = self.stream.cuda_stream
@@ -349,7 +365,8 @@ class OneShotLink:
         self._c.flags = self.flags.data_ptr()
         self._c.words = self.words.data_ptr()
         self._c.spin_limit = spin_limit
-        self.init()
+        if init:
+            self.init()
 
     def init(self) -> None:
         """Zero the counters and words (synchronizes the link's stream)."""

@@ -1,6 +1,7 @@
 """Ranks as processes on one GPU (mamba-rs src/dist/reducer.rs: the owner-shard
 dataflow of reduce_sum_fixed_order_nccl, with the process boundary the
-transport path has).
+transport path has; memra-engine tests/tp_ar_gpu.rs: the one-shot arm, one
+kernel per rank).
 
 Each of W processes (W = 2 or 4) is a rank owning one arena; the arenas are
 shared between the processes through device memory handles (torch's IPC
@@ -9,6 +10,11 @@ directly through the mapped handles (fold_slots over [arena_0, ...] at the
 shard), then writes its reduced shard into the other ranks' arenas.  A CPU barrier
 (gloo, host-side only) separates the phases.  Every arena must end equal to the
 oracle's fold of the original arenas, bit for bit.
+
+The one-shot test gives each of two processes its own rank's one-shot kernel
+(detfold_one_shot_rank); the staging buffers, barrier counters and refusal
+words are shared the same way, and the two kernels meet only through those
+counters.  Three rounds must double the sum twice, with both words zero.
 """
 import os
 import socket
@@ -75,3 +81,54 @@ def test_processes_fold_through_shared_arenas(detfold_lib, world, n):
     for r in range(world):
         got = arenas[r].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
+
+
+def _one_shot_rank_main(rank, xs, buffers, n, rounds, port, world):
+    import sys
+    import torch
+    import torch.distributed as dist
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import deterministic_fixed_order_amd as df
+
+    os.environ["MASTER_ADDR"] = "127.0.0.1"
+    os.environ["MASTER_PORT"] = str(port)
+    dist.init_process_group("gloo", rank=rank, world_size=world)
+    try:
+        torch.cuda.set_device(0)
+        link = df.OneShotLink(n, device="cuda:0", buffers=buffers, init=False)
+        for _ in range(rounds):
+            dist.barrier()  # both ranks launch their kernel within moments of each other
+            link.rank(rank, xs[rank], stream=link.stream)
+            torch.cuda.synchronize()
+        dist.barrier()
+    finally:
+        dist.destroy_process_group()
+
+
+@pytest.mark.parametrize("n", [4096, 65536])
+def test_one_shot_ranks_as_processes(detfold_lib, n):
+    # The one-shot arm in its per-rank shape: each process launches its own
+    # rank's kernel; the stage buffers, the barrier counters and the words are
+    # shared through device memory handles.  Every wait in the kernel is
+    # bounded, so a late peer can only produce a refusal word, never a hang.
+    import torch
+    import torch.multiprocessing as mp
+
+    rounds = 3
+    ha, hb = fold_inputs.vecf(n, 11 + n), fold_inputs.vecf(n, 77 + n)
+    want = oracle.fold_into(ha, hb)
+    for _ in range(rounds - 1):
+        want = oracle.fold_into(want, want)
+    dev = torch.device("cuda:0")
+    link = detfold_lib.OneShotLink(n, device=dev)  # zeroes the counters and words
+    xs = [torch.from_numpy(ha).to(dev), torch.from_numpy(hb).to(dev)]
+    torch.cuda.synchronize()
+    print("case: one-shot ranks as 2 processes, n=%d, %d rounds" % (n, rounds), flush=True)
+    mp.spawn(_one_shot_rank_main, args=(xs, (link.stage, link.flags, link.words), n, rounds,
+                                        _free_port(), 2), nprocs=2, join=True)
+    assert link.barrier_words() == [0, 0]
+    for r in range(2):
+        got = xs[r].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "rank %d, n=%d" % (r, n)
