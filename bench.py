@@ -221,6 +221,9 @@ def bench_fold(args, torch, df, dev):
         "algorithmic_bytes_per_launch": bytes_per_step,
         "avg_launch_ms": round(ms_per_step, 6),
     }
+    if args.alternate and inv_w is None:
+        result["alternating_arenas"] = bench_alternating(args, torch, df, dev, timer, stacked, out,
+                                                         bytes_per_step)
     if singles:
         result["scrubbed_single_launch"] = {
             "median_ms": round(statistics.median(singles), 6),
@@ -234,6 +237,37 @@ def bench_fold(args, torch, df, dev):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step)
     return result
+
+
+def bench_alternating(args, torch, df, dev, timer, stacked, out, bytes_per_step):
+    """The same fold, alternating between the arena and a separately allocated
+    copy of it (with its own output): each step's operands were last touched
+    two folds earlier, with a whole other arena read in between, so the
+    memory-side last-level cache can hold none of them when the step starts.
+    A rate close to the back-to-back one shows the latter is not cache-fed."""
+    stacked2 = stacked.clone()
+    out2 = torch.empty_like(out)
+    pair = [(out, stacked), (out2, stacked2)]
+    state = [0]
+
+    def step():
+        o, s = pair[state[0] & 1]
+        state[0] += 1
+        df.fold_ranks(o, s)
+
+    for _ in range(4):
+        step()
+    torch.cuda.synchronize()
+    steps = args.steps - (args.steps & 1)
+    ms = timer.region(step, steps) / steps
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int32), out2.view(torch.int32)))
+    del stacked2, out2
+    gbs = bytes_per_step / (ms * 1e-3) / 1e9
+    log("alternating two arenas: %.3f ms per step, %.1f GB/s (outputs equal: %s)" % (ms, gbs, same))
+    return {"ms_per_step": round(ms, 6), "GBps": round(gbs, 2), "steps": steps,
+            "outputs_equal": same,
+            "note": "two separately allocated copies of the arena, folded in turn"}
 
 
 def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
@@ -572,6 +606,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-alternate", dest="alternate", action="store_false",
+                    help="skip the two-arena control run")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
