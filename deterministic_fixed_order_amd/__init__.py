@@ -138,10 +138,24 @@ def _check(rc: int, what: str) -> None:
         raise DetfoldError(rc, what)
 
 
+_raw_current_stream = None
+
+
 def _stream_handle(t, stream) -> int:
+    """The hipStream_t to enqueue on: `stream` if given, else the caller's
+    current stream on t's device.  torch's raw accessor returns the handle
+    directly (0.1 us against 2 us for building a Stream object); the public
+    call is the fallback where it is missing."""
+    global _raw_current_stream
+    if stream is not None:
+        return int(stream.cuda_stream)
+    if _raw_current_stream is None:
+        import torch
+        _raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_current_stream:
+        return int(_raw_current_stream(t.device.index))
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream(t.device)
-    return int(s.cuda_stream)
+    return int(torch.cuda.current_stream(t.device).cuda_stream)
 
 
 def _f32_device(t, name: str) -> None:
