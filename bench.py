@@ -391,6 +391,17 @@ def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
     bit_exact = bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
     log("cpu oracle: %d runs, median %.3f s (%.2f GB/s); GPU output bit-exact: %s"
         % (len(times), med, bytes_per_step / med / 1e9, bit_exact))
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    threaded = None
+    if inv_w is None and threads > 1:
+        got_t, med_t, runs_t = oracle_threaded(host, threads, args.cpu_seconds / 2)
+        same = bool(np.array_equal(got_t.view(np.uint32), want.view(np.uint32)))
+        threaded = {"value": round(bytes_per_step / med_t / 1e9, 3), "unit": "GB/s", "cores": threads,
+                    "runs": runs_t, "bit_identical_to_single_thread": same,
+                    "sample": "the same arena split into %d contiguous element ranges, one thread "
+                              "each running the serial oracle on its range" % threads}
+        log("cpu oracle on %d threads: median %.3f s (%.2f GB/s); bits equal to one thread: %s"
+            % (threads, med_t, bytes_per_step / med_t / 1e9, same))
     return {
         "value": round(bytes_per_step / med / 1e9, 3),
         "unit": "GB/s",
@@ -400,7 +411,43 @@ def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
         "cpu_model": cpu_model(),
         "host_cpus_available": len(os.sched_getaffinity(0)),
         "gpu_output_bit_exact_vs_oracle": bit_exact,
+        "threaded": threaded,
     }
+
+
+def oracle_threaded(host, threads, seconds):
+    """The serial oracle, unchanged, on `threads` host threads at once: thread t
+    folds elements [n*t/T, n*(t+1)/T) through the oracle's separate-slots entry
+    (the C call releases the interpreter lock).  Returns the concatenated result,
+    the median time of one full fold and the number of timed runs."""
+    import threading
+    import numpy as np
+    import oracle
+
+    W, n = host.shape
+    bounds = [(n * t // threads, n * (t + 1) // threads) for t in range(threads)]
+    parts = [None] * threads
+
+    def work(t):
+        a, b = bounds[t]
+        parts[t] = oracle.fold([host[r, a:b] for r in range(W)])
+
+    def once():
+        pool = [threading.Thread(target=work, args=(t,)) for t in range(threads)]
+        for th in pool:
+            th.start()
+        for th in pool:
+            th.join()
+        return np.concatenate(parts)
+
+    got = once()
+    times = []
+    t_start = time.perf_counter()
+    while (time.perf_counter() - t_start < seconds or len(times) < 3) and len(times) < 5000:
+        t0 = time.perf_counter()
+        once()
+        times.append(time.perf_counter() - t0)
+    return got, statistics.median(times), len(times)
 
 
 def bench_join_only(args, torch, df, dev):

@@ -398,3 +398,28 @@ def test_pins_reject_scale_before_sum():
     with np.errstate(over="ignore", invalid="ignore"):
         failed = _pin_failures(oracle.fold_stacked, scaled)
     assert failed
+
+
+def test_oracle_on_disjoint_ranges_equals_the_whole_fold():
+    # the host oracle run on contiguous element ranges (as the threaded CPU
+    # baseline does, one range per thread) gives the whole fold's bits: the
+    # chain is per element, so the split cannot matter
+    import threading
+    W, n = 7, 100_003
+    host = fold_inputs.slots("varied", W, n, 91, spread=3.0)
+    want = oracle.fold_stacked(host)
+    T = 5
+    bounds = [(n * t // T, n * (t + 1) // T) for t in range(T)]
+    parts = [None] * T
+
+    def work(t):
+        a, b = bounds[t]
+        parts[t] = oracle.fold([host[r, a:b] for r in range(W)])
+
+    pool = [threading.Thread(target=work, args=(t,)) for t in range(T)]
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join()
+    got = np.concatenate(parts)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
