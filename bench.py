@@ -21,6 +21,7 @@ and the 16 KiB in-place fold latency.  Other modes (not the headline):
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -36,7 +37,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
 METRIC = "fold GB/s (W+1 bufs moved) and % HBM peak at W=8, 64 MiB/slot; 16 KiB latency"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fold_w8_64mib_hbm_counters.md")
-KERNEL_SRC = os.path.join(ROOT, "deterministic_fixed_order_amd", "csrc", "detfold.hip")
+LIB_SOURCES = sorted(glob.glob(os.path.join(ROOT, "deterministic_fixed_order_amd", "csrc", "*.hip")) +
+                     glob.glob(os.path.join(ROOT, "deterministic_fixed_order_amd", "csrc", "*.cpp")) +
+                     glob.glob(os.path.join(ROOT, "deterministic_fixed_order_amd", "csrc", "*.h"))) + \
+    [os.path.join(ROOT, "include", "detfold.h")]
 
 WORKLOADS = {
     # name: (family, W, len, seed0, scaled inv_w or None, base offset in elements)
@@ -84,9 +88,13 @@ def code_text(src: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the kernel source's code (comments and layout excluded)."""
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
+    """sha256[:16] of the library's code: every source under csrc/ and the public
+    header, each by file name, comments and layout excluded."""
+    h = hashlib.sha256()
+    for path in LIB_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            h.update(os.path.basename(path).encode() + b"\n" + code_text(f.read()).encode() + b"\n")
+    return h.hexdigest()[:16]
 
 
 def log(msg: str) -> None:

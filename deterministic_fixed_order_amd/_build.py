@@ -1,5 +1,10 @@
 """Build step for ``libdetfold.so`` (hipcc, gfx950 only).
 
+Sources (``csrc/``): fold_kernels.hip (device code and its launches), plan.cpp
+(host-only planning and argument checks), detfold.cpp (call sequences and the
+C ABI), internal.h (their shared declarations).  exports.map limits the
+exported symbols to the C ABI of include/detfold.h.
+
 Flags that fix the fold's bits:
   -ffp-contract=off                 no fused multiply-add anywhere
   -fno-fast-math                    no reassociation of the add chain
@@ -15,7 +20,9 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "detfold.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, f) for f in ("fold_kernels.hip", "plan.cpp", "detfold.cpp")]
+EXPORTS_MAP = os.path.join(CSRC, "exports.map")
 HEADER = os.path.join(ROOT, "include", "detfold.h")
 LIB = os.path.join(PKG, "libdetfold.so")
 ARCH = "gfx950"
@@ -33,14 +40,15 @@ def flags() -> list[str]:
         "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wextra", "-Wno-unused-parameter",
-        "-I", os.path.join(ROOT, "include"),
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        "-Wl,--version-script=" + EXPORTS_MAP,
     ]
 
 
 def build_library(out: str = LIB, extra: list[str] | None = None) -> str:
-    """Compile ``csrc/detfold.hip`` into ``out`` (atomically replaced)."""
+    """Compile the sources into ``out`` (atomically replaced)."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + (extra or []) + ["-o", tmp, SRC]
+    cmd = [hipcc()] + flags() + (extra or []) + ["-o", tmp] + SOURCES
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -49,7 +57,7 @@ def build_library(out: str = LIB, extra: list[str] | None = None) -> str:
 def save_temps(outdir: str) -> None:
     """Keep the gfx950 assembly of this build (for reading our own ISA)."""
     os.makedirs(outdir, exist_ok=True)
-    cmd = [hipcc()] + flags() + ["-save-temps=obj", "-o", os.path.join(outdir, "libdetfold.so"), SRC]
+    cmd = [hipcc()] + flags() + ["-save-temps=obj", "-o", os.path.join(outdir, "libdetfold.so")] + SOURCES
     subprocess.run(cmd, check=True, cwd=outdir)
 
 

@@ -1,0 +1,138 @@
+// internal.h -- declarations shared by the translation units of libdetfold:
+// fold_kernels.hip (device code and its launches), plan.cpp (host-only
+// planning and argument checks) and detfold.cpp (device queries, call
+// sequencing and the C ABI).  Not installed; the public interface is
+// include/detfold.h.  Only the C ABI is exported from the library.
+#ifndef DETFOLD_INTERNAL_H
+#define DETFOLD_INTERNAL_H
+
+#include <cstdint>
+
+#include "detfold.h"
+
+namespace detfold_impl {
+
+constexpr int kMaxBlock = 1024;
+constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth path
+constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
+constexpr int kMaxRowsW = 16;      // widest fold the LDS row body takes (one wave per slot)
+constexpr int kWideWaves = 16;     // slots per pass of the wide row body (W > kMaxRowsW)
+constexpr int kWideKiB = 4;        // KiB of one slot each wave of the wide body streams per pass
+
+// KiB of one slot each wave of the LDS row body streams per tile: ceil(W/4)
+// for W >= 3, 8 for W = 2.  Measured on MI355X over W = 2..16 and 1/2/4/8 KiB
+// per wave: with every CU holding 32 waves (32/W workgroups), ceil(W/4) KiB
+// per wave keeps about 8 KiB of output tiles in flight per CU and was the
+// fastest or within 2% of it at W = 3, 4, 5, 6, 8 and 16 (W = 8: 7.1 TB/s at
+// 64 MiB per slot, against 6.4 TB/s at 8 KiB per wave).  Two-slot folds have
+// only two waves per workgroup and want long runs instead.
+constexpr int rows_kib_per_wave(int w)
+{
+    return w <= 2 ? 8 : (w + 3) / 4;
+}
+
+// Memory policy of a launch.
+//  kStream  the bandwidth path: every input byte is read once, so loads carry
+//           the non-temporal hint, and stores are written through the
+//           per-XCD L2 (scope bits sc0 sc1) instead of sitting there dirty
+//           until an eviction competes with the incoming loads.
+//  kCached  the decode-join path: no hints; its output is read again soon.
+enum Policy : int { kCached = 0, kStream = 1 };
+
+// The decode-join path: payloads up to kLatencyBytes per buffer are
+// launch-latency bound and their result is read again soon, so they take one
+// position per thread, one pass and no cache hints; larger payloads are
+// bandwidth bound and stream.  Copies up to kCopyCachedBytes take no cache
+// hints either (a decode-join push is read by the peer's fold right away).
+constexpr int64_t kLatencyBytes = 8 << 20;
+constexpr int64_t kCopyCachedBytes = 1 << 20;
+
+// One-shot two-rank all-reduce: workgroup size, payload floats per workgroup
+// before the DETFOLD_ONE_SHOT_BLOCKS cap, and the default poll limit of a
+// barrier wait (about a second).
+constexpr int kOneShotBlock = 256;
+constexpr int64_t kOneShotPerBlock = 1024;
+constexpr int32_t kDefaultSpinLimit = 1 << 20;
+
+// Slot base pointers of the LDS row body, passed by value in the kernel
+// arguments (slot r of a stacked arena is stacked + r*len; fold_slots takes
+// them from the caller).  Also the destination list of the copy kernel.
+struct SlotTable {
+    const float *p[kMaxRowsW];
+};
+
+// Kernel arguments of the one-shot all-reduce.
+struct OneShotArgs {
+    float *x[2];      // the ranks' partials, folded in place
+    float *stage[2];  // stage[r]: where the peer's partial lands for rank r
+    uint32_t *flags;  // [entry|exit][rank][DETFOLD_ONE_SHOT_BLOCKS] counters
+    int32_t *words;   // per-rank barrier word
+    int64_t n;
+    int64_t chunk;    // floats per workgroup, a multiple of 4
+    int32_t blocks;   // workgroups per rank
+    int32_t rank0;    // rank of workgroups [0, blocks); a two-rank launch adds rank 1 after them
+    int32_t spin_limit;
+    int32_t vec;      // every buffer 16-byte aligned: 16-byte accesses
+};
+
+// The addresses and sizes one fold works on (host side, plain integers).
+struct Geometry {
+    uintptr_t out, s0, s1;  // byte addresses
+    int64_t stride;         // elements between slots r and r+1 for r >= 1
+    int32_t w;
+    int64_t len;
+    // Every slot's base address when the slots are not one stacked arena
+    // (fold_slots); otherwise empty and derived from s0, s1 and stride.
+    bool has_table = false;
+    uintptr_t table[kMaxRowsW] = {};
+
+    uintptr_t slot(int32_t r) const
+    {
+        if (has_table)
+            return table[r];
+        return r == 0 ? s0 : s1 + (uintptr_t)((r - 1) * stride) * 4;
+    }
+};
+
+// Offset of an address modulo 16 bytes, in floats.
+inline int phase16(uintptr_t a) { return (int)((a >> 2) & 3); }
+
+// --- plan.cpp: host only, no device access ---------------------------------
+bool vector_legal(const Geometry &g);
+int rows_block(int32_t w);
+int64_t rows_tile(int32_t w);
+int check_override(const detfold_launch *o);
+int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, int policy,
+              detfold_plan *p);
+int plan_into(const Geometry &g, int32_t cu_count, detfold_plan *p);
+bool ranges_overlap(uintptr_t a, uint64_t a_bytes, uintptr_t b, uint64_t b_bytes);
+int check_ranks_args(const float *out, const float *stacked, int32_t W, int64_t len);
+int check_into_args(const float *dst, const float *stage, int64_t n);
+int check_slots_args(const float *out, const float *const *slots, int32_t W, int64_t len);
+Geometry ranks_geometry(uintptr_t out, uintptr_t stacked, int32_t W, int64_t len);
+Geometry into_geometry(uintptr_t dst, uintptr_t stage, int64_t n);
+Geometry slots_geometry(const float *out, const float *const *slots, int32_t W, int64_t len);
+int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length);
+int check_round_args(float *const *arenas, int32_t W, int64_t n, const float *stage,
+                     int64_t stage_elems, int32_t flags);
+int check_pair_args(const detfold_pair_link *k, const float *x0, const float *x1, int64_t n);
+int check_link_events(const detfold_pair_link *k);
+bool bad_buffer(const void *p, int64_t n);
+int check_one_shot_link(const detfold_one_shot_link *k);
+int check_one_shot_buffers(const detfold_one_shot_link *k, const float *const *x, int nx, int64_t n);
+OneShotArgs one_shot_args(const detfold_one_shot_link *k, int32_t rank0, int nranks, float *xa,
+                          float *xb, int64_t n);
+
+// --- fold_kernels.hip: launches (hipStream_t and hipEvent_t passed as void*) -
+// With `done`, the event is recorded by the dispatch itself when the kernel
+// completes.  Each returns DETFOLD_OK or DETFOLD_ELAUNCH.
+int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv_w, void *stream,
+                void *done = nullptr);
+int launch_copy(float *const *dsts, int ndst, const float *src, int64_t len, int32_t cu,
+                void *stream, void *done = nullptr);
+int launch_one_shot(const OneShotArgs &a, int nranks, void *stream);
+int launch_zero_words(uint32_t *p, int64_t n, void *stream);
+
+}  // namespace detfold_impl
+
+#endif  // DETFOLD_INTERNAL_H

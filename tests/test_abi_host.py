@@ -37,6 +37,15 @@ def test_library_exports_every_declared_function(detfold_lib):
     assert set(detfold_lib.EXPORTS) == set(_declared_functions())
 
 
+def test_library_exports_nothing_but_the_c_abi(detfold_lib):
+    # the link's version script keeps every internal symbol local
+    import subprocess
+    res = subprocess.run(["nm", "-D", "--defined-only", detfold_lib.LIB_PATH], capture_output=True,
+                         text=True, check=True)
+    exported = {line.split()[-1] for line in res.stdout.splitlines() if line.strip()}
+    assert exported == set(_declared_functions())
+
+
 def test_abi_version(detfold_lib):
     assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 5
 

@@ -33,9 +33,9 @@ def isa(tmp_path_factory):
         _build.save_temps(out)
     except (OSError, subprocess.CalledProcessError) as e:  # pragma: no cover - no hipcc
         pytest.skip("hipcc build failed: %s" % e)
-    files = glob.glob(os.path.join(out, "*gfx950*.s"))
+    files = sorted(glob.glob(os.path.join(out, "*gfx950*.s")))
     assert files, "no gfx950 assembly produced"
-    return open(files[0]).read()
+    return "\n".join(open(f).read() for f in files)
 
 
 def _kernels(text):
