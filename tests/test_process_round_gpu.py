@@ -98,6 +98,11 @@ def _one_shot_rank_main(rank, xs, buffers, n, rounds, port, world):
     try:
         torch.cuda.set_device(0)
         link = df.OneShotLink(n, device="cuda:0", buffers=buffers, init=False)
+        # load the library's code object before the first barrier, so the
+        # peer's kernel never waits through this process's first launch
+        warm = torch.zeros(8, device="cuda:0")
+        df.fold_into(warm[:4], warm[4:])
+        torch.cuda.synchronize()
         for _ in range(rounds):
             dist.barrier()  # both ranks launch their kernel within moments of each other
             link.rank(rank, xs[rank], stream=link.stream)
