@@ -533,3 +533,25 @@ def test_wide_arena_rows_equal_direct_and_oracle(env, W, n, off):
         out.fill_(float("nan"))
         df.fold_ranks_ex(out, stacked, path=path)
         _assert_bits(_host(out), want, "W=%d path %d" % (W, path))
+
+
+@pytest.mark.parametrize("W", [100, 257])
+@pytest.mark.parametrize("n", [1, 3, 5, 1027, 70001])
+@pytest.mark.parametrize("off", [0, 1])
+def test_very_wide_folds_at_small_and_ragged_lengths(env, W, n, off):
+    # many passes of 16 slots (7 and 17 here, the last one partial), lengths
+    # that are all head and tail, one tile, or several tiles and a tail
+    df, torch, dev = env
+    host = fold_inputs.slots("mixed", W, n, 8100 + W + n)
+    want = oracle.fold_stacked(host)
+    want_s = oracle.fold_stacked_scaled(host, np.float32(0.5))
+    alloc = torch.empty(W * n + 4, dtype=torch.float32, device=dev)
+    stacked = alloc[off:off + W * n].view(W, n)
+    stacked.copy_(torch.from_numpy(host))
+    out = torch.empty(n + 4, dtype=torch.float32, device=dev)[(3 * off) % 4:(3 * off) % 4 + n]
+    _say("case: very wide W=%d n=%d off=%d" % (W, n, off))
+    out.fill_(float("nan"))
+    df.fold_ranks(out, stacked)
+    _assert_bits(_host(out), want, "W=%d n=%d off=%d" % (W, n, off))
+    df.fold_ranks_scaled(out, stacked, 0.5)
+    _assert_bits(_host(out), want_s, "W=%d n=%d off=%d scaled" % (W, n, off))
