@@ -78,6 +78,7 @@ def test_processes_fold_through_shared_arenas(detfold_lib, world, n):
     torch.cuda.synchronize()
     print("case: %d processes, n=%d" % (world, n), flush=True)
     mp.spawn(_rank_main, args=(arenas, n, _free_port(), world), nprocs=world, join=True)
+    torch.cuda.ipc_collect()  # release the handles the children held
     for r in range(world):
         got = arenas[r].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
@@ -133,6 +134,7 @@ def test_one_shot_ranks_as_processes(detfold_lib, n):
     print("case: one-shot ranks as 2 processes, n=%d, %d rounds" % (n, rounds), flush=True)
     mp.spawn(_one_shot_rank_main, args=(xs, (link.stage, link.flags, link.words), n, rounds,
                                         _free_port(), 2), nprocs=2, join=True)
+    torch.cuda.ipc_collect()
     assert link.barrier_words() == [0, 0]
     for r in range(2):
         got = xs[r].cpu().numpy()
