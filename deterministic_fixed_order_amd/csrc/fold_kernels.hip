@@ -230,27 +230,30 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
     fold_tiles<WS, U, float, SCALED, POL>(out, s0, s1, stride, w, len, inv_w);
 }
 
-// LDS row-transpose body (2 <= W <= 16).  One workgroup of W waves folds a
-// tile of T 16-byte groups of `out`: wave r streams the tile's bytes of slot r
-// -- LPW consecutive KiB, one contiguous run per wave -- straight into LDS row
-// r (buffer loads with the lds bit, no register staging); after a barrier
-// every thread folds whole groups from the W rows, in ascending row order, and
-// stores them.  Streaming one slot per wave keeps each wave on one run of HBM
-// rows; the direct body instead has every wave touch W runs 1 KiB at a time,
-// which measured 3-8% slower on MI355X.
+// LDS row-transpose body (2 <= W <= 16).  One workgroup of W/SPW waves folds
+// a tile of T 16-byte groups of `out`: wave q streams the tile's bytes of its
+// SPW slots q*SPW .. q*SPW+SPW-1 -- LPW consecutive KiB of each, one
+// contiguous run per slot -- straight into LDS rows (buffer loads with the lds
+// bit, no register staging); after a barrier every thread folds whole groups
+// from the W rows, in ascending row order, and stores them.  SPW is 1 except
+// for the eight-slot shape with two slots per wave (see rows_kib_per_wave).
+// Streaming whole runs of a slot keeps each wave on few runs of HBM rows; the
+// direct body instead has every wave touch W runs 1 KiB at a time, which
+// measured 3-8% slower on MI355X.
 //
 // Slot phases: the tile of `out` starts 16-byte aligned, but slot r's bytes
-// for the tile may start at any dword.  Wave r's buffer descriptor is based at
-// exactly that dword (gfx9 buffer loads need only dword alignment), so every
+// for the tile may start at any dword.  The buffer descriptor of slot r is
+// based at exactly that dword (gfx9 buffer loads need only dword alignment), so every
 // row lands in LDS aligned to the tile whatever the slot's phase, and the
 // fold reads 16-byte groups from every row alike.  The descriptor's range is
 // the tile's bytes of the slot, so no lane reads past them.  Measured on
 // MI355X against realigning shifted rows in LDS (one extra KiB loaded per
 // wave, 4-byte LDS reads): +3% at W=16 x 10,000,019 at base+1, +10% at W=7,
 // no change when every slot is aligned.
-template <int W> struct RowsShape {
-    static constexpr int LPW = rows_kib_per_wave(W);  // KiB each wave streams per tile
-    static constexpr int T = LPW * 64;                // 16-byte groups per tile
+template <int W, int SPW> struct RowsShape {
+    static constexpr int LPW = rows_kib_per_wave(W, SPW);  // KiB of each slot a wave streams per tile
+    static constexpr int T = LPW * 64;                     // 16-byte groups per tile
+    static constexpr int WAVES = W / SPW;                  // wave q streams slots q*SPW .. q*SPW+SPW-1
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -268,11 +271,12 @@ __device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slot
     out[i] = acc;
 }
 
-template <int W, bool SCALED>
-__global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
-                                                      int64_t head, float inv_w)
+template <int W, int SPW, bool SCALED>
+__global__ __launch_bounds__(W / SPW * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
+                                                            int64_t head, float inv_w)
 {
-    constexpr int LPW = RowsShape<W>::LPW, T = RowsShape<W>::T;
+    constexpr int LPW = RowsShape<W, SPW>::LPW, T = RowsShape<W, SPW>::T;
+    constexpr int NT = RowsShape<W, SPW>::WAVES * 64;  // threads per workgroup
     __shared__ f4 rows[W][T];
 
     const int64_t groups = (len - head) >> 2;
@@ -282,22 +286,25 @@ __global__ __launch_bounds__(W * 64) void k_fold_rows(float *out, SlotTable slot
         fold_one_table<W, SCALED>(out, slots, gid < head ? gid : tail0 + (gid - head), inv_w);
 
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's slot
-    const float *slot = slots.p[r];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;  // first element of the tile; out + e0 is 16-byte aligned
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot + e0, (uint32_t)(cnt * 16));
 #pragma unroll
-        for (int u = 0; u < LPW; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
-                                                     (uint32_t)(u * 64 + lane) * 16u, 0, 0,
-                                                     Aux<kStream>::load);
+        for (int j = 0; j < SPW; ++j) {  // this wave's slots
+            const uint32_t r = wave * SPW + j;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
+#pragma unroll
+            for (int u = 0; u < LPW; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
+                                                         (uint32_t)(u * 64 + lane) * 16u, 0, 0,
+                                                         Aux<kStream>::load);
+        }
         __syncthreads();  // every row has landed
 
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + e0, (uint32_t)(cnt * 16));
-        for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += W * 64) {
+        for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += NT) {
             f4 acc = rows[0][t];
 #pragma unroll
             for (int q = 1; q < W; ++q)
@@ -562,24 +569,24 @@ scalar_kernel_t pick_scalar_w(int unroll, int policy)
 typedef void (*rows_kernel_t)(float *, SlotTable, int64_t, int64_t, float);
 
 template <bool SCALED>
-rows_kernel_t pick_rows(int32_t w)
+rows_kernel_t pick_rows(int32_t w, int spw)
 {
     switch (w) {
-    case 2: return k_fold_rows<2, SCALED>;
-    case 3: return k_fold_rows<3, SCALED>;
-    case 4: return k_fold_rows<4, SCALED>;
-    case 5: return k_fold_rows<5, SCALED>;
-    case 6: return k_fold_rows<6, SCALED>;
-    case 7: return k_fold_rows<7, SCALED>;
-    case 8: return k_fold_rows<8, SCALED>;
-    case 9: return k_fold_rows<9, SCALED>;
-    case 10: return k_fold_rows<10, SCALED>;
-    case 11: return k_fold_rows<11, SCALED>;
-    case 12: return k_fold_rows<12, SCALED>;
-    case 13: return k_fold_rows<13, SCALED>;
-    case 14: return k_fold_rows<14, SCALED>;
-    case 15: return k_fold_rows<15, SCALED>;
-    default: return k_fold_rows<16, SCALED>;
+    case 2: return k_fold_rows<2, 1, SCALED>;
+    case 3: return k_fold_rows<3, 1, SCALED>;
+    case 4: return k_fold_rows<4, 1, SCALED>;
+    case 5: return k_fold_rows<5, 1, SCALED>;
+    case 6: return k_fold_rows<6, 1, SCALED>;
+    case 7: return k_fold_rows<7, 1, SCALED>;
+    case 8: return spw == 2 ? k_fold_rows<8, 2, SCALED> : k_fold_rows<8, 1, SCALED>;
+    case 9: return k_fold_rows<9, 1, SCALED>;
+    case 10: return k_fold_rows<10, 1, SCALED>;
+    case 11: return k_fold_rows<11, 1, SCALED>;
+    case 12: return k_fold_rows<12, 1, SCALED>;
+    case 13: return k_fold_rows<13, 1, SCALED>;
+    case 14: return k_fold_rows<14, 1, SCALED>;
+    case 15: return k_fold_rows<15, 1, SCALED>;
+    default: return k_fold_rows<16, 1, SCALED>;
     }
 }
 
@@ -645,7 +652,8 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
         e = launch(k, grid, block, args, stream, done);
     } else if (p.path == DETFOLD_PATH_ROWS) {
-        rows_kernel_t k = scaled ? pick_rows<true>(w) : pick_rows<false>(w);
+        const int spw = 64 * w / p.block;  // the plan's workgroup has one wave per spw slots
+        rows_kernel_t k = scaled ? pick_rows<true>(w, spw) : pick_rows<false>(w, spw);
         SlotTable slots = {};
         for (int32_t r = 0; r < w; ++r)
             slots.p[r] = reinterpret_cast<const float *>(g.slot(r));

@@ -28,10 +28,28 @@ bool vector_legal(const Geometry &g)
     return true;
 }
 
+// Slots each wave of the row body streams: two for an eight-slot fold unless
+// it is a stacked arena whose slot length is a multiple of kOneSlotAlign,
+// one otherwise.
+int rows_slots_per_wave(const Geometry &g)
+{
+    if (g.w != 8)
+        return 1;
+    return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
+}
+
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per
-// slot up to 16 slots, 16 waves making passes over the slots beyond that.
-int rows_block(int32_t w) { return w <= kMaxRowsW ? 64 * w : 64 * kWideWaves; }
-int64_t rows_tile(int32_t w) { return (int64_t)(w <= kMaxRowsW ? rows_kib_per_wave(w) : kWideKiB) * 64; }
+// one or two slots up to 16 slots, 16 waves making passes over the slots
+// beyond that.
+int rows_block(const Geometry &g)
+{
+    return g.w <= kMaxRowsW ? 64 * g.w / rows_slots_per_wave(g) : 64 * kWideWaves;
+}
+
+int64_t rows_tile(const Geometry &g)
+{
+    return (int64_t)(g.w <= kMaxRowsW ? rows_kib_per_wave(g.w, rows_slots_per_wave(g)) : kWideKiB) * 64;
+}
 
 // Positions per thread per pass.  The vector body moves 16 bytes per slot per
 // position, and one position per thread keeps the most waves in flight (the
@@ -95,7 +113,7 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
     if (path == DETFOLD_PATH_VECTOR && !vec_ok)
         return DETFOLD_EINVAL;
     if (path == DETFOLD_PATH_ROWS &&
-        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && o.block != rows_block(g.w)) ||
+        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && o.block != rows_block(g)) ||
          o.unroll > 1))
         return DETFOLD_EINVAL;
 
@@ -115,8 +133,8 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
     }
     if (path == DETFOLD_PATH_ROWS) {
         p->unroll = 1;
-        p->block = rows_block(g.w);
-        p->tile = rows_tile(g.w);
+        p->block = rows_block(g);
+        p->tile = rows_tile(g);
     } else {
         p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
         int block = o.block;

@@ -43,8 +43,12 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len)
         if ((int64_t)p->head + 4 * p->body + p->tail != len)
             fail("head + body + tail != len", W, len);
     }
-    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * W : 1024))
+    /* eight slots of a stacked arena: two slots per wave unless len is a multiple of 2^24 */
+    const int spw = (W == 8 && len % ((int64_t)1 << 24) != 0) ? 2 : 1;
+    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * W / spw : 1024))
         fail("row body with the wrong workgroup size", W, len);
+    if (p->path == DETFOLD_PATH_ROWS && W == 8 && p->tile != (spw == 2 ? 64 : 128))
+        fail("eight-slot row body with the wrong tile", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W < 2)
         fail("row body for one slot", W, len);
 }

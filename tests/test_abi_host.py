@@ -128,11 +128,31 @@ def test_plan_w8_64mib_per_slot(detfold_lib):
 @pytest.mark.parametrize("W,kib", [(2, 8), (3, 1), (4, 1), (5, 2), (7, 2), (8, 2), (9, 3),
                                    (12, 3), (13, 4), (16, 4)])
 def test_plan_rows_tile_per_width(detfold_lib, W, kib):
-    n = 1 << 22
-    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), W, n, CU)
+    n = 1 << 24  # a multiple of 2^24: one slot per wave at every width
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 32), W, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
     assert p["block"] == 64 * W and p["tile"] == 64 * kib  # kib KiB of each slot per wave
     assert p["grid"] == -(-(n // 4) // p["tile"])
+
+
+@pytest.mark.parametrize("n,spw", [(1 << 24, 1), (1 << 25, 1), (3 << 24, 1), (1 << 22, 2), (1 << 23, 2),
+                                   ((1 << 24) + 4, 2), (10_000_000, 2), (12_000_001, 2), (1 << 26, 1)])
+def test_plan_eight_slot_shape_follows_the_slot_length(detfold_lib, n, spw):
+    # W = 8: one slot per wave (8 waves x 2 KiB) when the slot length is a
+    # multiple of 2^24 floats, else two slots per wave (4 waves x 1 KiB each)
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU)
+    assert p["path"] == detfold_lib.PATH_ROWS
+    assert (p["block"], p["tile"]) == ((512, 128) if spw == 1 else (256, 64))
+    assert p["grid"] == -(-p["body"] // p["tile"])
+    # an override must name the shape's own workgroup size
+    bad = 256 if spw == 1 else 512
+    with pytest.raises(detfold_lib.DetfoldError):
+        detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU,
+                                    dict(path=detfold_lib.PATH_ROWS, block=bad, grid=0, unroll=0, policy=0))
+    # other widths keep one slot per wave at any length
+    for W in (4, 7, 16):
+        q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), W, n, CU)
+        assert q["block"] == 64 * W
 
 
 @pytest.mark.parametrize("W", [1, 17, 24])
@@ -219,13 +239,14 @@ def test_plan_override(detfold_lib):
     # the unhinted policy has only the direct bodies
     assert p["policy"] == detfold_lib.POLICY_CACHED and p["unroll"] == 1
     assert p["path"] == detfold_lib.PATH_VECTOR
+    # 2^20 is not a multiple of 2^24: the eight-slot row body with two slots per wave
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 30), 8, n, CU,
-                                    dict(path=detfold_lib.PATH_ROWS, block=512, grid=5, unroll=1,
+                                    dict(path=detfold_lib.PATH_ROWS, block=256, grid=5, unroll=1,
                                          policy=0))
-    assert (p["path"], p["block"], p["grid"], p["tile"]) == (detfold_lib.PATH_ROWS, 512, 5, 128)
+    assert (p["path"], p["block"], p["grid"], p["tile"]) == (detfold_lib.PATH_ROWS, 256, 5, 64)
 
 
-@pytest.mark.parametrize("W,launch", [(8, dict(block=256)), (8, dict(unroll=2)),
+@pytest.mark.parametrize("W,launch", [(8, dict(block=512)), (8, dict(unroll=2)),
                                       (8, dict(policy=2)), (1, {}), (17, dict(block=512)),
                                       (24, dict(unroll=2))])
 def test_plan_rejects_impossible_row_overrides(detfold_lib, W, launch):

@@ -280,8 +280,9 @@ def test_geometry_independence(env, W):
     stacked = _to_dev(torch, dev, host)
     out = torch.empty(n, dtype=torch.float32, device=dev)
     geoms = list(GEOMS)
-    if W >= 2:  # the LDS row bodies; block -1 stands for their own size, 64*W or 1024 beyond 16
-        rb = 64 * W if W <= 16 else 1024
+    if W >= 2:  # the LDS row bodies; block -1 stands for the size the plan gives them
+        cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        rb = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)["block"]
         geoms += [dict(g, block=rb if g["block"] < 0 else 0) for g in ROW_GEOMS]
     for geom in geoms:
         if W >= 16 and geom["unroll"] == 4 and geom["block"] == 1024:
@@ -296,7 +297,7 @@ def test_geometry_independence(env, W):
 
 @pytest.mark.parametrize("out_off,in_off", [(0, 0), (1, 1), (2, 2), (3, 3), (0, 1), (3, 0), (2, 1)])
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 4099, 4100, 65536 + 3])
-@pytest.mark.parametrize("W", [1, 2, 4, 7, 19])
+@pytest.mark.parametrize("W", [1, 2, 4, 7, 8, 19])
 def test_alignment_phases_and_ragged_lengths(env, out_off, in_off, n, W):
     df, torch, dev = env
     host = fold_inputs.slots("mixed", W, n, 7 * n + W)
