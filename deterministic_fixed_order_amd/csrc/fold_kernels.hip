@@ -236,7 +236,8 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
 // contiguous run per slot -- straight into LDS rows (buffer loads with the lds
 // bit, no register staging); after a barrier every thread folds whole groups
 // from the W rows, in ascending row order, and stores them.  SPW is 1 except
-// for the eight-slot shape with two slots per wave (see rows_kib_per_wave).
+// for the eight- and sixteen-slot shapes that stream several slots per wave
+// (see rows_kib_per_wave).
 // Streaming whole runs of a slot keeps each wave on few runs of HBM rows; the
 // direct body instead has every wave touch W runs 1 KiB at a time, which
 // measured 3-8% slower on MI355X.
@@ -586,7 +587,7 @@ rows_kernel_t pick_rows(int32_t w, int spw)
     case 13: return k_fold_rows<13, 1, SCALED>;
     case 14: return k_fold_rows<14, 1, SCALED>;
     case 15: return k_fold_rows<15, 1, SCALED>;
-    default: return k_fold_rows<16, 1, SCALED>;
+    default: return spw == 4 ? k_fold_rows<16, 4, SCALED> : k_fold_rows<16, 1, SCALED>;
     }
 }
 

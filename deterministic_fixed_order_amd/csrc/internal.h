@@ -31,11 +31,15 @@ constexpr int rows_kib_per_wave(int w)
     return w <= 2 ? 8 : (w + 3) / 4;
 }
 
-// Eight-slot folds have a second shape: four waves, each streaming 1 KiB of
-// two slots per tile (the same bytes per wave and per CU, half the tile).
-// Measured on MI355X over 20 slot lengths, it is 1.5-12% faster wherever the
-// slot length is not a multiple of 2^24 floats, and 0.8-1.4% slower where it
-// is (2^24, 2^25, 2^26), whose 64 MiB-aligned runs the one-slot shape suits.
+// Eight- and sixteen-slot folds have a second shape, in which each wave
+// streams 1 KiB of several slots per tile (SPW slots per wave; the plan picks
+// it, see rows_slots_per_wave).  Measured on MI355X:
+//  * W = 8, two slots per wave (four waves): 1.5-12% faster wherever the slot
+//    length is not a multiple of 2^24 floats, 0.8-1.4% slower where it is
+//    (2^24, 2^25, 2^26), whose 64 MiB-aligned runs the one-slot shape suits;
+//  * W = 16, four slots per wave (four waves): 0-30% faster when every slot
+//    shares out's 16-byte phase (14 lengths, never below -0.5%), 3-12% slower
+//    at 5 of 6 lengths when the slots are shifted.
 // The shapes differ only in which wave loads which slot; every element's
 // chain is the same.
 constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot lengths at this multiple

@@ -28,14 +28,17 @@ bool vector_legal(const Geometry &g)
     return true;
 }
 
-// Slots each wave of the row body streams: two for an eight-slot fold unless
-// it is a stacked arena whose slot length is a multiple of kOneSlotAlign,
-// one otherwise.
+// Slots each wave of the row body streams: for eight slots two, unless they
+// are a stacked arena whose slot length is a multiple of kOneSlotAlign; for
+// sixteen slots four when every slot shares out's 16-byte phase; one
+// otherwise.
 int rows_slots_per_wave(const Geometry &g)
 {
-    if (g.w != 8)
-        return 1;
-    return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
+    if (g.w == 8)
+        return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
+    if (g.w == 16)
+        return vector_legal(g) ? 4 : 1;
+    return 1;
 }
 
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per

@@ -21,7 +21,7 @@ static void fail(const char *what, int64_t w, int64_t len)
 }
 
 /* What a kernel launch needs from a plan. */
-static void check_plan(const detfold_plan *p, int32_t W, int64_t len)
+static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coaligned)
 {
     if (len == 0) {
         if (p->grid != 0)
@@ -43,12 +43,15 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len)
         if ((int64_t)p->head + 4 * p->body + p->tail != len)
             fail("head + body + tail != len", W, len);
     }
-    /* eight slots of a stacked arena: two slots per wave unless len is a multiple of 2^24 */
-    const int spw = (W == 8 && len % ((int64_t)1 << 24) != 0) ? 2 : 1;
+    /* eight slots of a stacked arena: two slots per wave unless len is a multiple of 2^24;
+     * sixteen: four slots per wave when every slot shares out's 16-byte phase */
+    const int spw = (W == 8 && len % ((int64_t)1 << 24) != 0) ? 2 : (W == 16 && coaligned) ? 4 : 1;
     if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * W / spw : 1024))
         fail("row body with the wrong workgroup size", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W == 8 && p->tile != (spw == 2 ? 64 : 128))
         fail("eight-slot row body with the wrong tile", W, len);
+    if (p->path == DETFOLD_PATH_ROWS && W == 16 && p->tile != (spw == 4 ? 64 : 256))
+        fail("sixteen-slot row body with the wrong tile", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W < 2)
         fail("row body for one slot", W, len);
 }
@@ -103,7 +106,9 @@ int main(void)
                             sum = sum * 31 + (uint64_t)rc;
                             if (rc == DETFOLD_OK) {
                                 ++accepted;
-                                check_plan(&plan, W, len);
+                                const int co = ((out >> 2) & 3) == ((st >> 2) & 3) && (out & 3) == 0 &&
+                                               (st & 3) == 0 && len % 4 == 0;
+                                check_plan(&plan, W, len, co);
                                 sum = sum * 31 + (uint64_t)plan.grid + (uint64_t)plan.path;
                             } else if (rc != DETFOLD_EINVAL && rc != DETFOLD_EOVERLAP) {
                                 fail("unexpected return code", W, len);
@@ -120,7 +125,7 @@ int main(void)
                     ++calls;
                     if (rc == DETFOLD_OK) {
                         ++accepted;
-                        check_plan(&plan, 2, lens[li]);
+                        check_plan(&plan, 2, lens[li], 0);
                     }
                 }
 

@@ -128,8 +128,10 @@ def test_plan_w8_64mib_per_slot(detfold_lib):
 @pytest.mark.parametrize("W,kib", [(2, 8), (3, 1), (4, 1), (5, 2), (7, 2), (8, 2), (9, 3),
                                    (12, 3), (13, 4), (16, 4)])
 def test_plan_rows_tile_per_width(detfold_lib, W, kib):
-    n = 1 << 24  # a multiple of 2^24: one slot per wave at every width
-    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 32), W, n, CU)
+    # a slot length that is a multiple of 2^24 and slots shifted 4 bytes from
+    # out's 16-byte phase: one slot per wave at every width
+    n = 1 << 24
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 32) + 4, W, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
     assert p["block"] == 64 * W and p["tile"] == 64 * kib  # kib KiB of each slot per wave
     assert p["grid"] == -(-(n // 4) // p["tile"])
@@ -149,8 +151,8 @@ def test_plan_eight_slot_shape_follows_the_slot_length(detfold_lib, n, spw):
     with pytest.raises(detfold_lib.DetfoldError):
         detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU,
                                     dict(path=detfold_lib.PATH_ROWS, block=bad, grid=0, unroll=0, policy=0))
-    # other widths keep one slot per wave at any length
-    for W in (4, 7, 16):
+    # other widths keep one slot per wave at any length (sixteen: see below)
+    for W in (4, 7, 12):
         q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), W, n, CU)
         assert q["block"] == 64 * W
 
@@ -451,3 +453,17 @@ def test_plan_wide_rows(detfold_lib, W, n):
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 36), W, n, CU,
                                     dict(path=detfold_lib.PATH_ROWS, block=1024, grid=3, unroll=0, policy=0))
     assert (p["block"], p["grid"]) == (1024, 3)
+
+
+@pytest.mark.parametrize("n", [1 << 22, 1 << 24, 3 << 20, 6_000_000, 10_000_000, 10_000_019])
+def test_plan_sixteen_slot_shape_follows_alignment(detfold_lib, n):
+    # W = 16: four slots per wave (4 waves x 1 KiB each) when out and every
+    # slot share one 16-byte phase, one slot per wave (16 waves x 4 KiB) else
+    aligned = n % 4 == 0
+    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 16, n, CU)
+    assert (p["block"], p["tile"]) == ((256, 64) if aligned else (1024, 256))
+    q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, 16, n, CU)  # slot 0 shifted
+    assert (q["block"], q["tile"]) == (1024, 256)
+    for plan in (p, q):
+        assert plan["path"] == detfold_lib.PATH_ROWS
+        assert plan["grid"] == -(-plan["body"] // plan["tile"])

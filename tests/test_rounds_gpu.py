@@ -105,6 +105,24 @@ def test_fold_slots_in_place_and_repeated_slots(env, W):
     _assert_bits(_host(torch, out), oracle.fold([host[0], host[1], host[0]]), "repeated slot")
 
 
+@pytest.mark.parametrize("W", [8, 16])
+@pytest.mark.parametrize("n", [5, 4096, 70001, 1 << 20])
+def test_fold_slots_co_aligned_takes_the_many_slots_per_wave_shape(env, W, n):
+    # every buffer at one 16-byte phase: the eight- and sixteen-slot row
+    # bodies stream several slots per wave; out of place and in place
+    df, torch, dev = env
+    host = fold_inputs.slots("varied", W, n, 700 + W + n, spread=3.0)
+    want = oracle.fold([host[r] for r in range(W)])
+    for phase in (0, 2):
+        slots = [_placed(torch, dev, host[r], phase) for r in range(W)]
+        out = _placed(torch, dev, np.full(n, np.nan, np.float32), phase)
+        _say("case: co-aligned fold_slots W=%d n=%d phase %d" % (W, n, phase))
+        df.fold_slots(out, slots)
+        _assert_bits(_host(torch, out), want, "W=%d n=%d phase %d" % (W, n, phase))
+        df.fold_slots(slots[W - 1], slots)  # in place on the last slot
+        _assert_bits(_host(torch, slots[W - 1]), want, "W=%d n=%d phase %d in place" % (W, n, phase))
+
+
 # --------------------------------------------------------------------------
 # the one-GPU reduction round
 
