@@ -318,23 +318,24 @@ __global__ __launch_bounds__(W / SPW * 64) void k_fold_rows(float *out, SlotTabl
     }
 }
 
-// Wide LDS row body (W > 16, stacked arena): a workgroup of 16 waves folds a
-// tile of 256 groups in passes of 16 slots.  In pass p wave q streams 4 KiB of
-// slot 16p + q into LDS row q, exactly as the row body above does; after the
-// barrier the thread that owns group t continues its chain with rows 0, 1, ...
-// of the pass -- pass 0 starts it from slot 0 -- and a second barrier frees
-// the rows for the next pass.  The running sum stays in the thread's
-// registers between passes, so each element still sees the adds in strictly
-// ascending slot order, one rounding each, and is stored once at the end.
-template <bool SCALED>
-__global__ __launch_bounds__(kWideWaves * 64) void k_fold_rows_wide(float *out, const float *s0,
-                                                                    const float *s1, int64_t stride,
-                                                                    int w, int64_t len, int64_t head,
-                                                                    float inv_w)
+// Wide LDS row body (W > 16, stacked arena): a workgroup of WAVES waves folds
+// a tile of KIB*64 groups in passes of 16 slots.  In pass p wave q streams KIB
+// KiB of each of its SPW slots 16p + q*SPW + j into LDS row q*SPW + j, as the
+// row body above does; after the barrier the thread that owns group t
+// continues its chain with rows 0, 1, ... of the pass -- pass 0 starts it
+// from slot 0 -- and a second barrier frees the rows for the next pass.  The
+// running sum stays in the thread's registers between passes, so each element
+// still sees the adds in strictly ascending slot order, one rounding each,
+// and is stored once at the end.
+template <int WAVES, int SPW, int KIB, bool SCALED>
+__global__ __launch_bounds__(WAVES * 64) void k_fold_rows_wide(float *out, const float *s0,
+                                                               const float *s1, int64_t stride, int w,
+                                                               int64_t len, int64_t head, float inv_w)
 {
-    constexpr int T = kWideKiB * 64;  // groups per tile, at most one per thread
-    static_assert(T <= kWideWaves * 64, "one group per thread");
-    __shared__ f4 rows[kWideWaves][T];
+    constexpr int T = KIB * 64;  // groups per tile, at most one per thread
+    static_assert(T <= WAVES * 64, "one group per thread");
+    static_assert(WAVES * SPW == kWideSlots, "a pass is 16 slots");
+    __shared__ f4 rows[kWideSlots][T];
 
     const int64_t groups = (len - head) >> 2;
     const int64_t tail0 = head + (groups << 2);
@@ -350,17 +351,21 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_fold_rows_wide(float *out, 
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int base = 0; base < w; base += kWideWaves) {
-            const int nr = w - base < kWideWaves ? w - base : kWideWaves;
-            if (wave < nr) {
-                const int r = base + wave;
-                const float *slot = r == 0 ? s0 : s1 + (int64_t)(r - 1) * stride;
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot + e0, (uint32_t)(cnt * 16));
+        for (int base = 0; base < w; base += kWideSlots) {
+            const int nr = w - base < kWideSlots ? w - base : kWideSlots;
 #pragma unroll
-                for (int u = 0; u < kWideKiB; ++u)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[wave][u * 64], 16,
-                                                             (uint32_t)(u * 64 + lane) * 16u, 0, 0,
-                                                             Aux<kStream>::load);
+            for (int j = 0; j < SPW; ++j) {  // this wave's slots of the pass
+                const int q = wave * SPW + j;
+                if (q < nr) {
+                    const int r = base + q;
+                    const float *slot = r == 0 ? s0 : s1 + (int64_t)(r - 1) * stride;
+                    const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot + e0, (uint32_t)(cnt * 16));
+#pragma unroll
+                    for (int u = 0; u < KIB; ++u)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[q][u * 64], 16,
+                                                                 (uint32_t)(u * 64 + lane) * 16u, 0, 0,
+                                                                 Aux<kStream>::load);
+                }
             }
             __syncthreads();  // this pass's rows have landed
             if (t < (uint32_t)cnt) {
@@ -649,7 +654,13 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
     const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
     hipError_t e;
     if (p.path == DETFOLD_PATH_ROWS && w > kMaxRowsW) {
-        const void *k = scaled ? (const void *)k_fold_rows_wide<true> : (const void *)k_fold_rows_wide<false>;
+        // the plan's workgroup size names the pass shape
+        const bool aligned = p.block == 64 * kWideAlignedWaves;
+        constexpr int AW = kWideAlignedWaves, AS = kWideSlots / kWideAlignedWaves, AK = kWideAlignedKiB;
+        const void *k = aligned ? (scaled ? (const void *)k_fold_rows_wide<AW, AS, AK, true>
+                                          : (const void *)k_fold_rows_wide<AW, AS, AK, false>)
+                                : (scaled ? (const void *)k_fold_rows_wide<kWideWaves, 1, kWideKiB, true>
+                                          : (const void *)k_fold_rows_wide<kWideWaves, 1, kWideKiB, false>);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
         e = launch(k, grid, block, args, stream, done);
     } else if (p.path == DETFOLD_PATH_ROWS) {

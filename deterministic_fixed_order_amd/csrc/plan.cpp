@@ -42,16 +42,20 @@ int rows_slots_per_wave(const Geometry &g)
 }
 
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per
-// one or two slots up to 16 slots, 16 waves making passes over the slots
-// beyond that.
+// one, two or four slots up to 16 slots; beyond that, passes of 16 slots by
+// 16 waves (8 waves when every slot shares out's phase).
 int rows_block(const Geometry &g)
 {
-    return g.w <= kMaxRowsW ? 64 * g.w / rows_slots_per_wave(g) : 64 * kWideWaves;
+    if (g.w <= kMaxRowsW)
+        return 64 * g.w / rows_slots_per_wave(g);
+    return 64 * (vector_legal(g) ? kWideAlignedWaves : kWideWaves);
 }
 
 int64_t rows_tile(const Geometry &g)
 {
-    return (int64_t)(g.w <= kMaxRowsW ? rows_kib_per_wave(g.w, rows_slots_per_wave(g)) : kWideKiB) * 64;
+    if (g.w <= kMaxRowsW)
+        return (int64_t)rows_kib_per_wave(g.w, rows_slots_per_wave(g)) * 64;
+    return (int64_t)(vector_legal(g) ? kWideAlignedKiB : kWideKiB) * 64;
 }
 
 // Positions per thread per pass.  The vector body moves 16 bytes per slot per

@@ -249,7 +249,7 @@ def test_plan_override(detfold_lib):
 
 
 @pytest.mark.parametrize("W,launch", [(8, dict(block=512)), (8, dict(unroll=2)),
-                                      (8, dict(policy=2)), (1, {}), (17, dict(block=512)),
+                                      (8, dict(policy=2)), (1, {}), (17, dict(block=256)),
                                       (24, dict(unroll=2))])
 def test_plan_rejects_impossible_row_overrides(detfold_lib, W, launch):
     cfg = dict(path=detfold_lib.PATH_ROWS, block=0, grid=0, unroll=0, policy=0)
@@ -443,14 +443,17 @@ def test_one_shot_rejects_bad_arguments(detfold_lib):
 @pytest.mark.parametrize("W", [17, 24, 32, 33, 64, 100])
 @pytest.mark.parametrize("n", [1 << 22, 10_000_019, 4099])
 def test_plan_wide_rows(detfold_lib, W, n):
-    # beyond 16 slots: 16 waves making passes of 16 slots over 256-group tiles
+    # beyond 16 slots: passes of 16 slots -- 8 waves x 2 slots x 1 KiB over
+    # 64-group tiles when out and every slot share one 16-byte phase, else
+    # 16 waves x 1 slot x 4 KiB over 256-group tiles
     for out, stacked in ((BASE, BASE + (1 << 36)), (BASE + 4, BASE + (1 << 36) + 12)):
+        aligned = out % 16 == stacked % 16 and n % 4 == 0
         p = detfold_lib.plan_fold_ranks(out, stacked, W, n, CU)
         assert p["path"] == detfold_lib.PATH_ROWS
-        assert (p["block"], p["tile"], p["unroll"]) == (1024, 256, 1)
-        assert p["grid"] == max(1, -(-p["body"] // 256))
+        assert (p["block"], p["tile"], p["unroll"]) == ((512, 64, 1) if aligned else (1024, 256, 1))
+        assert p["grid"] == max(1, -(-p["body"] // p["tile"]))
         assert p["head"] + 4 * p["body"] + p["tail"] == n
-    p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 36), W, n, CU,
+    p = detfold_lib.plan_fold_ranks(BASE + 4, BASE + (1 << 36) + 12, W, n, CU,
                                     dict(path=detfold_lib.PATH_ROWS, block=1024, grid=3, unroll=0, policy=0))
     assert (p["block"], p["grid"]) == (1024, 3)
 

@@ -537,11 +537,12 @@ def test_wide_arena_rows_equal_direct_and_oracle(env, W, n, off):
 
 
 @pytest.mark.parametrize("W", [100, 257])
-@pytest.mark.parametrize("n", [1, 3, 5, 1027, 70001])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1027, 1028, 70000, 70001])
 @pytest.mark.parametrize("off", [0, 1])
 def test_very_wide_folds_at_small_and_ragged_lengths(env, W, n, off):
     # many passes of 16 slots (7 and 17 here, the last one partial), lengths
-    # that are all head and tail, one tile, or several tiles and a tail
+    # that are all head and tail, one tile, or several tiles and a tail; the
+    # co-aligned cases (off 0, n a multiple of 4) take the 8-wave pass shape
     df, torch, dev = env
     host = fold_inputs.slots("mixed", W, n, 8100 + W + n)
     want = oracle.fold_stacked(host)
