@@ -283,8 +283,9 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
     p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
     if p["path"] == df.PATH_ROWS and W > 16:
-        return "k_fold_rows_wide<%s> grid=%d block=%d tile=%d" % (
-            str(scaled).lower(), p["grid"], p["block"], p["tile"])
+        shape = "16,1,4" if p["block"] == 1024 else "8,2,1"  # waves, slots per wave, KiB
+        return "k_fold_rows_wide<%s,%s> grid=%d block=%d tile=%d" % (
+            shape, str(scaled).lower(), p["grid"], p["block"], p["tile"])
     if p["path"] == df.PATH_ROWS:
         return "k_fold_rows<%d,%d,%s> grid=%d block=%d tile=%d" % (
             W, 64 * W // p["block"], str(scaled).lower(), p["grid"], p["block"], p["tile"])
