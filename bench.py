@@ -13,7 +13,11 @@ prints one JSON line: metric, value (GB/s of algorithmic bytes), the roofline
 of the fold kernel, the CPU oracle timed on the host as a reported baseline,
 and the 16 KiB in-place fold latency.  Other modes (not the headline):
 
-    --workload {w8,w4,w16,join}   other configurations, same JSON shape
+    --workload {w8,w4,w16,w32}    other fold configurations, same JSON shape
+    --workload {join,round,pair,procs}
+                                  the in-place fold's latency, the one-GPU
+                                  round, two ranks on two streams, and ranks
+                                  as processes sharing device memory
     --sweep                       launch-geometry sweep of the headline fold
     --copy-calibration            a plain device copy of known size, for
                                   scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
@@ -57,6 +61,8 @@ WORKLOAD_NAMES = {
     "join": "fold_into n=4096 f32 (16 KiB per buffer)",
     "round": "loopback_round W=8 arenas of 16777216 f32 (64 MiB each), staged and direct",
     "pair": "two-stream pair all-reduce at the decode-join sizes",
+    "procs": "ranks as processes: W=4 arenas of 16777216 f32 shared by device memory handles; "
+             "one-shot ranks at n=4096",
 }
 
 
@@ -652,12 +658,181 @@ def copy_calibration(args, torch, dev):
             "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+PROCS_W, PROCS_N, PROCS_SHOT_N = 4, 1 << 24, 4096
+
+
+def _free_port() -> int:
+    import socket
+    with socket.socket(socket.AF_INET, socket.SOCK_STREAM) as so:
+        so.bind(("127.0.0.1", 0))
+        return so.getsockname()[1]
+
+
+def _procs_join(rank, world, port):
+    import torch.distributed as dist
+    root = os.path.dirname(os.path.abspath(__file__))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    os.environ["MASTER_ADDR"] = "127.0.0.1"
+    os.environ["MASTER_PORT"] = str(port)
+    dist.init_process_group("gloo", rank=rank, world_size=world)
+    return dist
+
+
+def _procs_fold_main(rank, arenas, want, steps, warmup, port, results):
+    """Rank `rank`: time its owner-shard fold over the mapped arenas, in turn."""
+    import torch
+    world = len(arenas)
+    dist = _procs_join(rank, world, port)
+    try:
+        import deterministic_fixed_order_amd as df
+        torch.cuda.set_device(0)
+        start, length = df.shard_plan(arenas[0].numel(), world)[rank]
+        slots = [a[start:start + length] for a in arenas]
+        out = torch.empty(length, dtype=torch.float32, device="cuda:0")
+        timer = Timer(torch, torch.cuda.current_stream())
+        for turn in range(world):
+            dist.barrier()  # one rank folds at a time; the others wait on the host
+            if turn != rank:
+                continue
+            for _ in range(warmup):
+                df.fold_slots(out, slots)
+            results[rank] = timer.region(lambda: df.fold_slots(out, slots), steps) / steps
+            same = torch.equal(out.view(torch.int32), want[start:start + length].view(torch.int32))
+            results[world + rank] = 1.0 if same else 0.0
+        dist.barrier()
+    finally:
+        dist.destroy_process_group()
+
+
+def _procs_shot_main(rank, xs, buffers, calls, delay_cycles, port, results):
+    """Rank `rank` of the one-shot link: `calls` back-to-back rank kernels,
+    queued behind a delay kernel so that they run without host gaps."""
+    import torch
+    dist = _procs_join(rank, 2, port)
+    try:
+        import deterministic_fixed_order_amd as df
+        torch.cuda.set_device(0)
+        n = xs[rank].numel()
+        link = df.OneShotLink(n, device="cuda:0", buffers=buffers, init=False,
+                              stream=torch.cuda.Stream(device="cuda:0"))
+        for _ in range(20):  # the code object is loaded and both sides are in step
+            dist.barrier()
+            link.rank(rank, xs[rank], stream=link.stream)
+            link.stream.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        dist.barrier()
+        with torch.cuda.stream(link.stream):
+            torch.cuda._sleep(delay_cycles)  # bounded spin; the calls queue up behind it
+            start.record(link.stream)
+            for _ in range(calls):
+                link.rank(rank, xs[rank], stream=link.stream)
+            end.record(link.stream)
+        end.synchronize()
+        results[rank] = start.elapsed_time(end) * 1e3 / calls  # us per call
+        dist.barrier()
+    finally:
+        dist.destroy_process_group()
+
+
+def bench_procs(args, torch, df, dev):
+    """Ranks as processes on one GPU.
+
+    Fold: PROCS_W processes share PROCS_W arenas of PROCS_N floats (allocated
+    by this process, mapped by each child through device memory handles).  In
+    turn, each rank times back-to-back folds of its owner shard over all the
+    mapped arenas (fold_slots into a buffer of its own, the direct round's
+    phase A) while the others wait on a host barrier, and checks its result
+    against the same fold run here on the unmapped arenas, bit for bit.
+
+    One-shot: two processes, each launching its own rank's kernel
+    (detfold_one_shot_rank) at n = PROCS_SHOT_N; the kernels meet only through
+    the shared counters.  The calls are queued behind a bounded delay kernel
+    so that the device runs them back to back; the time per call is taken on
+    each rank from events around its calls (the rank whose delay ended first
+    also counts the wait for its peer's first kernel)."""
+    import torch.multiprocessing as mp
+    import fold_inputs
+
+    W, n = PROCS_W, PROCS_N
+    host = fold_inputs.slots("vecf", W, n, 1000)
+    arenas = [torch.from_numpy(host[r]).to(dev) for r in range(W)]
+    want = torch.empty(n, dtype=torch.float32, device=dev)
+    moved, local = [], []
+    timer = Timer(torch, torch.cuda.current_stream(dev))
+    for start, length in df.shard_plan(n, W):
+        slots = [a[start:start + length] for a in arenas]
+        df.fold_slots(want[start:start + length], slots)
+        out = torch.empty(length, dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            df.fold_slots(out, slots)
+        local.append(timer.region(lambda: df.fold_slots(out, slots), args.steps) / args.steps)
+        moved.append((W + 1) * length * 4)
+    torch.cuda.synchronize()
+
+    results = torch.zeros(2 * W, dtype=torch.float64).share_memory_()
+    log("procs: %d ranks fold their owner shards over mapped arenas" % W)
+    mp.spawn(_procs_fold_main, args=(arenas, want, args.steps, args.warmup, _free_port(), results),
+             nprocs=W, join=True)
+    torch.cuda.ipc_collect()
+    ranks = []
+    for r in range(W):
+        ms = float(results[r])
+        row = {"rank": r, "ms_per_fold": round(ms, 5), "GBps": round(moved[r] / (ms * 1e-3) / 1e9, 1),
+               "unmapped_ms_per_fold": round(local[r], 5),
+               "unmapped_GBps": round(moved[r] / (local[r] * 1e-3) / 1e9, 1),
+               "bits_equal_unmapped": bool(results[W + r] == 1.0)}
+        ranks.append(row)
+        log("rank %d: %.4f ms per owner fold (%.1f GB/s) over mapped arenas; %.4f ms (%.1f GB/s) "
+            "unmapped; bits equal %s" % (r, ms, row["GBps"], local[r], row["unmapped_GBps"],
+                                         row["bits_equal_unmapped"]))
+    if not all(x["bits_equal_unmapped"] for x in ranks):
+        raise RuntimeError("a rank's fold over mapped arenas differs from the unmapped fold")
+
+    m, calls = PROCS_SHOT_N, 500
+    link = df.OneShotLink(m, device=dev)  # zeroes the counters and the words
+    xs = [torch.zeros(m, dtype=torch.float32, device=dev) for _ in range(2)]
+    probe_cycles = 1 << 22
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    torch.cuda._sleep(probe_cycles)
+    t1.record()
+    t1.synchronize()
+    ms_per_cycle = t0.elapsed_time(t1) / probe_cycles
+    delay_cycles = int(20.0 / ms_per_cycle)  # about 20 ms: room to enqueue every call first
+    torch.cuda.synchronize()
+    shot = torch.zeros(2, dtype=torch.float64).share_memory_()
+    log("procs: one-shot rank kernels in 2 processes, n=%d, %d calls behind a %.1f ms delay"
+        % (m, calls, delay_cycles * ms_per_cycle))
+    mp.spawn(_procs_shot_main, args=(xs, (link.stage, link.flags, link.words), calls, delay_cycles,
+                                     _free_port(), shot), nprocs=2, join=True)
+    torch.cuda.ipc_collect()
+    words = link.barrier_words()
+    if words != [0, 0]:
+        raise RuntimeError("one-shot barrier words %s after the process calls" % words)
+    per_call = [round(float(shot[r]), 3) for r in range(2)]
+    log("one-shot ranks as processes: %s us per call (rank 0, rank 1)" % per_call)
+
+    ms_sum = sum(x["ms_per_fold"] for x in ranks)
+    return {
+        "metric": "ranks as processes: owner-shard folds over arenas shared by device memory handles",
+        "value": round(sum(moved) / (ms_sum * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_sum, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": WORKLOAD_NAMES["procs"], "W": W, "len": n},
+        "ranks": ranks,
+        "one_shot_processes": {"n": m, "calls": calls, "us_per_call": per_call, "barrier_words": words},
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join", "round", "pair"], default="w8")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join", "round", "pair", "procs"],
+                    default="w8")
     ap.add_argument("--singles", type=int, default=30, help="scrubbed single-launch samples")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -691,6 +866,8 @@ def main(argv=None) -> int:
         res = bench_round(args, torch, df, dev)
     elif args.workload == "pair":
         res = bench_pair(args, torch, df, dev)
+    elif args.workload == "procs":
+        res = bench_procs(args, torch, df, dev)
     else:
         res = bench_fold(args, torch, df, dev)
     res["kernel_source_sha256_16"] = kernel_source_hash()
