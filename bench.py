@@ -323,7 +323,7 @@ def bench_join(args, torch, df, dev, timer):
         for _ in range(20):
             df.fold_into(xa, stage)
         torch.cuda.synchronize()
-        reps = 500
+        reps = 1000
         b2b = timer.region(lambda: df.fold_into(xa, stage), reps) / reps
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(torch.cuda.current_stream(dev))
@@ -833,7 +833,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join", "round", "pair", "procs"],
                     default="w8")
-    ap.add_argument("--singles", type=int, default=30, help="scrubbed single-launch samples")
+    ap.add_argument("--singles", type=int, default=50, help="scrubbed single-launch samples")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
