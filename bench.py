@@ -59,7 +59,7 @@ WORKLOAD_NAMES = {
     "w16": "fold_ranks W=16 stacked [16][10000019] f32 at base+1 element, uniform [-1,1)",
     "w32": "fold_ranks W=32 stacked [32][8000001] f32 at base+1 element, uniform [-1,1)",
     "join": "fold_into n=4096 f32 (16 KiB per buffer)",
-    "round": "loopback_round W=8 arenas of 16777216 f32 (64 MiB each), staged and direct",
+    "round": "loopback_round W=8 arenas of 16777216 f32 (64 MiB each): staged, direct and fused",
     "pair": "two-stream pair all-reduce at the decode-join sizes",
     "procs": "ranks as processes: W=4 arenas of 16777216 f32 shared by device memory handles; "
              "one-shot ranks at n=4096",
@@ -485,7 +485,8 @@ def bench_round(args, torch, df, dev):
     Bytes moved per round (direct): each owner reads its shard of all W arenas
     and writes its own ((W+1)*n*4 over all owners), then every reduced shard is
     read once and written to the other W-1 arenas (W*n*4).  Staged adds the
-    gather copies into the stage (2*W*n*4)."""
+    gather copies into the stage (2*W*n*4).  Fused reads every arena once and
+    writes it once (2*W*n*4)."""
     import fold_inputs
 
     W, n = 8, 1 << 24
@@ -494,15 +495,15 @@ def bench_round(args, torch, df, dev):
     stage = torch.empty(df.round_stage_elems(n, W), dtype=torch.float32, device=dev)
     timer = Timer(torch, torch.cuda.current_stream(dev))
     res = {}
-    for mode in ("direct", "staged"):
-        direct = mode == "direct"
+    for mode in ("direct", "staged", "fused"):
+        direct, fused = mode == "direct", mode == "fused"
 
         def step():
-            df.loopback_round(arenas, None if direct else stage, direct=direct)
+            df.loopback_round(arenas, stage if mode == "staged" else None, direct=direct, fused=fused)
         for _ in range(args.warmup):
             step()
         ms = timer.region(step, args.steps) / args.steps
-        moved = (2 * W + 1) * n * 4 if direct else (4 * W + 1) * n * 4
+        moved = {"direct": (2 * W + 1) * n * 4, "staged": (4 * W + 1) * n * 4, "fused": 2 * W * n * 4}[mode]
         res[mode] = {"ms_per_round": round(ms, 4), "bytes_moved": moved,
                      "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
         log("round %s: %.3f ms per round, %.1f GB/s of bytes moved" % (mode, ms, res[mode]["GBps"]))

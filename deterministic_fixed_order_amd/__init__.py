@@ -13,7 +13,7 @@ PyTorch is used for device memory and streams only.
     fold_ranks_scaled(out, stacked, inv_w)   the same, then * inv_w
     fold_into(dst, stage)                    dst = dst + stage (in place)
     fold_slots(out, [s_0, ..., s_{W-1}])     the fold over separate buffers (W <= 16)
-    loopback_round(arenas, stage=None, ...)  one owner-shard reduction round over W arenas
+    loopback_round(arenas, stage=None, ...)  one reduction round over W arenas (staged, direct, fused)
     PairLink(...).all_reduce(x0, x1)         two-stream (two-rank) all-reduce on one device
     PairLink(...).broadcast / all_gather     pure movement between the two ranks
     OneShotLink(...).all_reduce(x0, x1)      the one-kernel arm with an in-kernel barrier
@@ -33,11 +33,11 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 ONE_SHOT_BLOCKS = 64
 ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
 BARRIER_ENTRY_EXPIRED, BARRIER_EXIT_EXPIRED = 40043, 40044
-ROUND_REVERSE_DELIVERY, ROUND_DIRECT = 1, 2
+ROUND_REVERSE_DELIVERY, ROUND_DIRECT, ROUND_FUSED = 1, 2, 4
 
 EXPORTS = (
     "fold_ranks", "fold_into", "fold_ranks_scaled", "detfold_strerror", "detfold_abi_version",
@@ -258,13 +258,15 @@ def round_stage_elems(n: int, world: int) -> int:
 
 
 def loopback_round(arenas, stage=None, *, reverse_delivery: bool = False, direct: bool = False,
-                   stream=None) -> None:
+                   fused: bool = False, stream=None) -> None:
     """One fixed-order reduction round across the W arenas (one device).
 
     Afterwards every arena holds the ascending-rank fold of all the arenas'
     previous contents.  Staged (default) gathers each owner's shard copies into
     ``stage`` (at least ``round_stage_elems(n, W)`` floats) before folding;
-    ``direct`` folds straight from the arenas."""
+    ``direct`` folds each owner's shard straight from the arenas, then
+    distributes it; ``fused`` does the whole round in one kernel that folds
+    every tile from the arenas and writes it back into all of them."""
     if not arenas:
         raise ValueError("need at least one arena")
     n = arenas[0].numel()
@@ -272,7 +274,8 @@ def loopback_round(arenas, stage=None, *, reverse_delivery: bool = False, direct
         _f32_device(a, "arenas[%d]" % i)
         if a.numel() != n:
             raise ValueError("arena %d has %d elements, arena 0 has %d" % (i, a.numel(), n))
-    flags = (ROUND_REVERSE_DELIVERY if reverse_delivery else 0) | (ROUND_DIRECT if direct else 0)
+    flags = ((ROUND_REVERSE_DELIVERY if reverse_delivery else 0) | (ROUND_DIRECT if direct else 0)
+             | (ROUND_FUSED if fused else 0))
     stage_ptr, stage_elems = None, 0
     if stage is not None:
         _f32_device(stage, "stage")

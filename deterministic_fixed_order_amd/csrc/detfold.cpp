@@ -97,8 +97,11 @@ int run_slots(float *out, const float *const *slots, int32_t W, int64_t len, boo
 // DETFOLD_ROUND_REVERSE_DELIVERY, descending source order, then fold_ranks
 // folds `stage`.  Direct: the owner folds straight from the W arenas
 // (fold_slots, in place on its own shard), since on one device every arena is
-// already in the same HBM.  Bytes move by device-to-device copies only, so the
-// bits are the fold's whatever the mode or the delivery order.
+// already in the same HBM.  Fused: no owner shards at all -- one kernel folds
+// every tile from the W arenas and writes the sum back into that tile of each
+// (k_fold_rows_all), the shape an owner takes when its peers' buffers are
+// mapped.  Bytes move by device-to-device copies only, so the bits are the
+// fold's whatever the mode or the delivery order.
 int run_round(float *const *arenas, int32_t W, int64_t n, float *stage, int32_t flags,
               hipStream_t stream)
 {
@@ -106,6 +109,13 @@ int run_round(float *const *arenas, int32_t W, int64_t n, float *stage, int32_t 
     int rc = current_cu_count(&cu);
     if (rc != DETFOLD_OK)
         return rc;
+    if (flags & DETFOLD_ROUND_FUSED) {
+        const Geometry g = slots_geometry(arenas[0], arenas, W, n);
+        detfold_plan p;
+        if ((rc = make_plan(g, cu, nullptr, DETFOLD_POLICY_STREAM, &p)) != DETFOLD_OK)
+            return rc;
+        return launch_rows_all(g, p, stream);
+    }
     int64_t start[kMaxRowsW], length[kMaxRowsW];
     balanced_shards(n, W, start, length);
     const bool direct = flags & DETFOLD_ROUND_DIRECT;

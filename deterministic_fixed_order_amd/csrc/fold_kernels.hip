@@ -318,6 +318,80 @@ __global__ __launch_bounds__(W / SPW * 64) void k_fold_rows(float *out, SlotTabl
     }
 }
 
+// Fold and write back (the fused one-device round, W <= 16 separate
+// buffers): every slot ends holding the fold of all.  The loads are the row
+// body's; then each thread that owns a group folds it in ascending row order
+// and leaves the sum in row 0, and after a second barrier wave q writes the
+// tile of row 0 into its own slots q*SPW .. q*SPW+SPW-1, through a descriptor
+// based at each slot's first element of the tile as its loads were, so any
+// 16-byte phase works.  A workgroup has read its tile of every slot (first
+// barrier) before it writes any of them, and workgroups own disjoint tiles;
+// the head and tail elements are read, folded and written back by one thread
+// each.  Every byte of every slot is read once and written once.
+template <int W, int SPW>
+__global__ __launch_bounds__(W / SPW * 64) void k_fold_rows_all(SlotTable slots, int64_t len,
+                                                                int64_t head)
+{
+    constexpr int LPW = RowsShape<W, SPW>::LPW, T = RowsShape<W, SPW>::T;
+    constexpr int NT = RowsShape<W, SPW>::WAVES * 64;  // threads per workgroup
+    __shared__ f4 rows[W][T];
+
+    const int64_t groups = (len - head) >> 2;
+    const int64_t tail0 = head + (groups << 2);
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < head + (len - tail0)) {
+        const int64_t i = gid < head ? gid : tail0 + (gid - head);
+        float acc = slots.p[0][i];
+#pragma unroll
+        for (int r = 1; r < W; ++r)
+            acc = acc + slots.p[r][i];
+#pragma unroll
+        for (int r = 0; r < W; ++r)
+            const_cast<float *>(slots.p[r])[i] = acc;
+    }
+
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
+        const int64_t g0 = tile * T;
+        const int64_t cnt = groups - g0 < T ? groups - g0 : T;
+        const int64_t e0 = head + 4 * g0;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const uint32_t r = wave * SPW + j;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
+#pragma unroll
+            for (int u = 0; u < LPW; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
+                                                         (uint32_t)(u * 64 + lane) * 16u, 0, 0,
+                                                         Aux<kStream>::load);
+        }
+        __syncthreads();  // every row has landed
+
+        for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += NT) {
+            f4 acc = rows[0][t];
+#pragma unroll
+            for (int q = 1; q < W; ++q)
+                acc = acc + rows[q][t];  // ascending slot order, one rounding per add
+            rows[0][t] = acc;
+        }
+        __syncthreads();  // the sums are in row 0
+
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const uint32_t r = wave * SPW + j;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) {
+                const uint32_t g = (uint32_t)(u * 64) + lane;
+                if (g < (uint32_t)cnt)
+                    bstore<Aux<kStream>::store>(rows[0][g], rs, g * 16u);
+            }
+        }
+        __syncthreads();  // row 0 is read before the next tile refills the rows
+    }
+}
+
 // Wide LDS row body (W > 16, stacked arena): a workgroup of WAVES waves folds
 // a tile of KIB*64 groups in passes of 16 slots.  In pass p wave q streams KIB
 // KiB of each of its SPW slots 16p + q*SPW + j into LDS row q*SPW + j, as the
@@ -592,7 +666,30 @@ rows_kernel_t pick_rows(int32_t w, int spw)
     case 13: return k_fold_rows<13, 1, SCALED>;
     case 14: return k_fold_rows<14, 1, SCALED>;
     case 15: return k_fold_rows<15, 1, SCALED>;
-    default: return spw == 4 ? k_fold_rows<16, 4, SCALED> : k_fold_rows<16, 1, SCALED>;
+    default: return spw == 2 ? k_fold_rows<16, 2, SCALED> : k_fold_rows<16, 1, SCALED>;
+    }
+}
+
+typedef void (*rows_all_kernel_t)(SlotTable, int64_t, int64_t);
+
+rows_all_kernel_t pick_rows_all(int32_t w, int spw)
+{
+    switch (w) {
+    case 2: return k_fold_rows_all<2, 1>;
+    case 3: return k_fold_rows_all<3, 1>;
+    case 4: return k_fold_rows_all<4, 1>;
+    case 5: return k_fold_rows_all<5, 1>;
+    case 6: return k_fold_rows_all<6, 1>;
+    case 7: return k_fold_rows_all<7, 1>;
+    case 8: return spw == 2 ? k_fold_rows_all<8, 2> : k_fold_rows_all<8, 1>;
+    case 9: return k_fold_rows_all<9, 1>;
+    case 10: return k_fold_rows_all<10, 1>;
+    case 11: return k_fold_rows_all<11, 1>;
+    case 12: return k_fold_rows_all<12, 1>;
+    case 13: return k_fold_rows_all<13, 1>;
+    case 14: return k_fold_rows_all<14, 1>;
+    case 15: return k_fold_rows_all<15, 1>;
+    default: return spw == 2 ? k_fold_rows_all<16, 2> : k_fold_rows_all<16, 1>;
     }
 }
 
@@ -683,6 +780,25 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
         e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
     }
     return e == hipSuccess ? DETFOLD_OK : DETFOLD_ELAUNCH;
+}
+
+// The fused round's launch: the plan of a fold over the slot table (row
+// body, 2 <= W <= 16), with k_fold_rows_all in place of k_fold_rows.
+int launch_rows_all(const Geometry &g, const detfold_plan &p, void *stream)
+{
+    if (p.path != DETFOLD_PATH_ROWS || !g.has_table || g.w < 2 || g.w > kMaxRowsW)
+        return DETFOLD_EINVAL;
+    const int spw = 64 * g.w / p.block;
+    rows_all_kernel_t k = pick_rows_all(g.w, spw);
+    SlotTable slots = {};
+    for (int32_t r = 0; r < g.w; ++r)
+        slots.p[r] = reinterpret_cast<const float *>(g.table[r]);
+    int64_t len = g.len, head = p.head;
+    void *args[] = {&slots, &len, &head};
+    return launch(reinterpret_cast<const void *>(k), dim3((unsigned)p.grid), dim3((unsigned)p.block), args,
+                  static_cast<hipStream_t>(stream), nullptr) == hipSuccess
+               ? DETFOLD_OK
+               : DETFOLD_ELAUNCH;
 }
 
 // Copy len floats from src to each of ndst destinations with k_copy_out.

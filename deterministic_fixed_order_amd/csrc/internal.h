@@ -42,9 +42,12 @@ constexpr int rows_kib_per_wave(int w)
 //  * W = 8, two slots per wave (four waves): 1.5-12% faster wherever the slot
 //    length is not a multiple of 2^24 floats, 0.8-1.4% slower where it is
 //    (2^24, 2^25, 2^26), whose 64 MiB-aligned runs the one-slot shape suits;
-//  * W = 16, four slots per wave (four waves): 0-30% faster when every slot
-//    shares out's 16-byte phase (14 lengths, never below -0.5%), 3-12% slower
-//    at 5 of 6 lengths when the slots are shifted.
+//  * W = 16, two slots per wave (eight waves): when every slot shares out's
+//    16-byte phase, 0.4-4.3% faster than four slots per wave (four waves) on
+//    the stacked fold at six lengths, 1.4-6% on separate slots, 2-16% on the
+//    fused round, and up to 30% faster than one slot per wave (16 waves x
+//    4 KiB); with shifted slots one slot per wave stays best (several slots
+//    per wave lose 3-12%).
 // The shapes differ only in which wave loads which slot; every element's
 // chain is the same.
 constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot lengths at this multiple
@@ -153,6 +156,9 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
                 void *done = nullptr);
 int launch_copy(float *const *dsts, int ndst, const float *src, int64_t len, int32_t cu,
                 void *stream, void *done = nullptr);
+// Every slot of a table geometry becomes the fold of all (the fused round);
+// `p` is the plan make_plan gives that geometry.
+int launch_rows_all(const Geometry &g, const detfold_plan &p, void *stream);
 int launch_one_shot(const OneShotArgs &a, int nranks, void *stream);
 int launch_zero_words(uint32_t *p, int64_t n, void *stream);
 

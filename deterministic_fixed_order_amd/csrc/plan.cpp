@@ -30,19 +30,19 @@ bool vector_legal(const Geometry &g)
 
 // Slots each wave of the row body streams: for eight slots two, unless they
 // are a stacked arena whose slot length is a multiple of kOneSlotAlign; for
-// sixteen slots four when every slot shares out's 16-byte phase; one
+// sixteen slots two when every slot shares out's 16-byte phase; one
 // otherwise.
 int rows_slots_per_wave(const Geometry &g)
 {
     if (g.w == 8)
         return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
     if (g.w == 16)
-        return vector_legal(g) ? 4 : 1;
+        return vector_legal(g) ? 2 : 1;
     return 1;
 }
 
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per
-// one, two or four slots up to 16 slots; beyond that, passes of 16 slots by
+// one or two slots up to 16 slots; beyond that, passes of 16 slots by
 // 16 waves (8 waves when every slot shares out's phase).
 int rows_block(const Geometry &g)
 {
@@ -284,7 +284,9 @@ int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length)
 int check_round_args(float *const *arenas, int32_t W, int64_t n, const float *stage,
                      int64_t stage_elems, int32_t flags)
 {
-    if (W < 1 || W > kMaxRowsW || n < 0 || (flags & ~(DETFOLD_ROUND_REVERSE_DELIVERY | DETFOLD_ROUND_DIRECT)))
+    constexpr int32_t known = DETFOLD_ROUND_REVERSE_DELIVERY | DETFOLD_ROUND_DIRECT | DETFOLD_ROUND_FUSED;
+    if (W < 1 || W > kMaxRowsW || n < 0 || (flags & ~known) ||
+        ((flags & DETFOLD_ROUND_FUSED) && flags != DETFOLD_ROUND_FUSED))
         return DETFOLD_EINVAL;
     if (W == 1 || n == 0)
         return DETFOLD_OK;
@@ -297,7 +299,7 @@ int check_round_args(float *const *arenas, int32_t W, int64_t n, const float *st
             if (ranges_overlap((uintptr_t)arenas[r], (uint64_t)n * 4, (uintptr_t)arenas[q], (uint64_t)n * 4))
                 return DETFOLD_EOVERLAP;
     }
-    if (!(flags & DETFOLD_ROUND_DIRECT)) {
+    if (!(flags & (DETFOLD_ROUND_DIRECT | DETFOLD_ROUND_FUSED))) {
         const int64_t need = (int64_t)W * ((n + W - 1) / W);
         if (!stage || (((uintptr_t)stage) & 3) || stage_elems < need)
             return DETFOLD_EINVAL;

@@ -140,18 +140,26 @@ int fold_slots_scaled(float *out, const float *const *slots, int32_t W, int64_t 
  *   n            elements per arena, >= 0
  *   stage        device scratch of at least W * ceil(n / W) floats, owned by
  *                the caller, overwritten; unused (may be NULL) with
- *                DETFOLD_ROUND_DIRECT
+ *                DETFOLD_ROUND_DIRECT or DETFOLD_ROUND_FUSED
  *   stage_elems  capacity of `stage` in floats
  *   flags        DETFOLD_ROUND_REVERSE_DELIVERY: gather the sources' shards
  *                into the stage in descending source order (slot placement is
  *                still by source rank, so the bits do not change);
  *                DETFOLD_ROUND_DIRECT: fold each owner's shard straight from
- *                the W arenas, with no stage and no gather copies
- * Errors: DETFOLD_EINVAL, DETFOLD_EOVERLAP (arenas overlap each other or the
- * stage), DETFOLD_EDEVICE, DETFOLD_ELAUNCH.  Stream-ordered; no synchronize.
+ *                the W arenas, with no stage and no gather copies;
+ *                DETFOLD_ROUND_FUSED: one kernel and no owner shards -- each
+ *                workgroup reads one tile of all W arenas, folds it and writes
+ *                the sum back into that tile of every arena, so each arena
+ *                byte is read once and written once (W*n*4 bytes each way).
+ *                Not combinable with the other flags; no stage.
+ * Arenas may sit at any 4-byte-aligned addresses (any 16-byte phases).
+ * Errors: DETFOLD_EINVAL (also for an unknown flag or FUSED with another
+ * flag), DETFOLD_EOVERLAP (arenas overlap each other or the stage),
+ * DETFOLD_EDEVICE, DETFOLD_ELAUNCH.  Stream-ordered; no synchronize.
  */
 #define DETFOLD_ROUND_REVERSE_DELIVERY 1
 #define DETFOLD_ROUND_DIRECT 2
+#define DETFOLD_ROUND_FUSED 4
 int detfold_loopback_round(float *const *arenas, int32_t W, int64_t n, float *stage,
                            int64_t stage_elems, int32_t flags, void *stream);
 
@@ -288,7 +296,7 @@ int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 5
+#define DETFOLD_ABI_VERSION 6
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------

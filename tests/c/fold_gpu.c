@@ -206,7 +206,7 @@ static void round_case(const char *name, int32_t W, int64_t n, int32_t flags, ui
         hs[r] = h[r];
     }
     const int64_t stage_elems = (int64_t)W * ((n + W - 1) / W);
-    float *stage = (flags & DETFOLD_ROUND_DIRECT) ? NULL : dev_alloc(stage_elems);
+    float *stage = (flags & (DETFOLD_ROUND_DIRECT | DETFOLD_ROUND_FUSED)) ? NULL : dev_alloc(stage_elems);
     expect_rc(name, detfold_loopback_round(d, W, n, stage, stage ? stage_elems : 0, flags, g_stream),
               DETFOLD_OK);
     HIP_OK(hipStreamSynchronize(g_stream));
@@ -336,6 +336,7 @@ int main(void)
     slots_case("fold_slots W=5 n=1027 mixed phases", 5, 1027, 9);
     round_case("loopback_round W=4 n=1001 direct", 4, 1001, DETFOLD_ROUND_DIRECT, 10);
     round_case("loopback_round W=4 n=1001 staged reversed", 4, 1001, DETFOLD_ROUND_REVERSE_DELIVERY, 11);
+    round_case("loopback_round W=8 n=70001 fused", 8, 70001, DETFOLD_ROUND_FUSED, 13);
     links_case(4096, 12);
 
     HIP_OK(hipStreamDestroy(g_stream));

@@ -47,7 +47,7 @@ def test_library_exports_nothing_but_the_c_abi(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 5
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 6
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -342,7 +342,10 @@ def test_loopback_round_rejects_bad_arguments(detfold_lib):
     assert lib.detfold_loopback_round(_ptrs(*[BASE + i * (1 << 20) for i in range(17)]), 17, n, stage,
                                       10 ** 6, 0, None) == EINVAL
     assert lib.detfold_loopback_round(_ptrs(*ar), 4, -1, stage, need, 0, None) == EINVAL
-    assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, stage, need, 4, None) == EINVAL     # unknown flag
+    assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, stage, need, 8, None) == EINVAL     # unknown flag
+    fused = detfold_lib.ROUND_FUSED
+    for other in (detfold_lib.ROUND_DIRECT, detfold_lib.ROUND_REVERSE_DELIVERY):
+        assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, None, 0, fused | other, None) == EINVAL
     assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, stage, need - 1, 0, None) == EINVAL  # stage short
     assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, None, 0, 0, None) == EINVAL
     assert lib.detfold_loopback_round(_ptrs(ar[0], ar[1], ar[1] + 8, ar[3]), 4, n, stage, need, 0,
@@ -350,9 +353,13 @@ def test_loopback_round_rejects_bad_arguments(detfold_lib):
     assert lib.detfold_loopback_round(_ptrs(*ar), 4, n, ar[2] + 100, need, 0, None) == EOVERLAP
     assert lib.detfold_loopback_round(_ptrs(*ar[:1]), 1, n, None, 0, 0, None) == OK        # one rank
     assert lib.detfold_loopback_round(_ptrs(*ar), 4, 0, None, 0, 0, None) == OK            # empty
-    # direct mode needs no stage, but still checks the arenas
-    assert lib.detfold_loopback_round(_ptrs(ar[0], ar[0], ar[2], ar[3]), 4, n, None, 0,
-                                      detfold_lib.ROUND_DIRECT, None) == EOVERLAP
+    # direct and fused modes need no stage, but still check the arenas
+    for mode in (detfold_lib.ROUND_DIRECT, fused):
+        assert lib.detfold_loopback_round(_ptrs(ar[0], ar[0], ar[2], ar[3]), 4, n, None, 0,
+                                          mode, None) == EOVERLAP
+        assert lib.detfold_loopback_round(_ptrs(ar[0], ar[1] + 2, ar[2], ar[3]), 4, n, None, 0,
+                                          mode, None) == EINVAL                     # misaligned arena
+    assert lib.detfold_loopback_round(_ptrs(*ar[:1]), 1, n, None, 0, fused, None) == OK    # one rank
 
 
 def test_pair_all_reduce_rejects_bad_arguments(detfold_lib):
@@ -460,11 +467,11 @@ def test_plan_wide_rows(detfold_lib, W, n):
 
 @pytest.mark.parametrize("n", [1 << 22, 1 << 24, 3 << 20, 6_000_000, 10_000_000, 10_000_019])
 def test_plan_sixteen_slot_shape_follows_alignment(detfold_lib, n):
-    # W = 16: four slots per wave (4 waves x 1 KiB each) when out and every
+    # W = 16: two slots per wave (8 waves x 1 KiB each) when out and every
     # slot share one 16-byte phase, one slot per wave (16 waves x 4 KiB) else
     aligned = n % 4 == 0
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 16, n, CU)
-    assert (p["block"], p["tile"]) == ((256, 64) if aligned else (1024, 256))
+    assert (p["block"], p["tile"]) == ((512, 64) if aligned else (1024, 256))
     q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, 16, n, CU)  # slot 0 shifted
     assert (q["block"], q["tile"]) == (1024, 256)
     for plan in (p, q):

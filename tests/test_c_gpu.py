@@ -24,7 +24,7 @@ def test_c_caller_on_the_device(detfold_lib):
     assert lines[-1] == "all ok"
     cases = [l[5:] for l in lines if l.startswith("case ")]
     oks = [l[3:] for l in lines if l.startswith("ok ")]
-    assert len(cases) == 14 and not any(l.startswith("FAIL") for l in lines)
+    assert len(cases) == 15 and not any(l.startswith("FAIL") for l in lines)
     for name in cases:
         if name not in ("pair link all-reduce", "one-shot all-reduce"):
             assert name in oks, name

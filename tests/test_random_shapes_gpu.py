@@ -4,7 +4,7 @@ of a hand-picked grid.
 
 Each case draws a width, a length, the 16-byte phases of the output and of
 the inputs, an input family and (for the stacked fold) the scale, so that the
-plan's choices -- LDS row body with one, two or four slots per wave, the wide
+plan's choices -- LDS row body with one or two slots per wave, the wide
 row body's two pass shapes, the direct bodies, head and tail lengths, one-pass
 grids of every size -- are crossed with each other far more often than a grid
 would.  Widths reach 70 (five passes of the wide row body), lengths reach

@@ -7,8 +7,8 @@ and the two-stream pair all-reduce (through the C ABI), against the oracle.
 * loopback_round: W arenas, each owner folds its shard, then distributes it
   (mamba-rs src/dist/reducer.rs, LoopbackWorld::run_round), staged with
   ascending and with reversed delivery order (the `reverse_delivery` flag),
-  and direct; every arena must end equal to the oracle's fold of all the
-  arenas, bit for bit.
+  direct, and fused into one fold-and-write-back kernel; every arena must end
+  equal to the oracle's fold of all the arenas, bit for bit.
 * pair all-reduce: two streams as two ranks, push into the peer's reused
   staging buffer, event-ordered fold (memra-engine tests/tp_ar_gpu.rs, ArLink
   pipeline arm): sweep n in {1, 4, 1024, 4096, 16384, 65536} and beyond,
@@ -136,14 +136,37 @@ def test_loopback_round_every_arena_holds_the_fold(env, W, n):
     host = fold_inputs.slots("vecf" if W in (8, 16) else "mixed", W, n, 3000 + 7 * W)
     want = oracle.fold_stacked(host)
     stage = torch.empty(df.round_stage_elems(n, W) + 1, dtype=torch.float32, device=dev)
-    for mode in ("ascending", "reversed", "direct"):
+    for mode in ("ascending", "reversed", "direct", "fused"):
         _say("case: loopback round W=%d n=%d %s" % (W, n, mode))
         # arenas at mixed 16-byte phases, each in its own allocation
         arenas = [_placed(torch, dev, host[r], (r + n) % 4) for r in range(W)]
-        df.loopback_round(arenas, None if mode == "direct" else stage[1:],
-                          reverse_delivery=(mode == "reversed"), direct=(mode == "direct"))
+        staged = mode in ("ascending", "reversed")
+        df.loopback_round(arenas, stage[1:] if staged else None, reverse_delivery=(mode == "reversed"),
+                          direct=(mode == "direct"), fused=(mode == "fused"))
         for r in range(W):
             _assert_bits(_host(torch, arenas[r]), want, "W=%d n=%d %s arena %d" % (W, n, mode, r))
+
+
+@pytest.mark.parametrize("W", [2, 4, 8, 16])
+@pytest.mark.parametrize("n", [1, 6, 4096, 70_001, 1 << 20])
+def test_fused_round_on_co_aligned_arenas(env, W, n):
+    # every arena at one 16-byte phase: the eight- and sixteen-arena rounds
+    # take the several-slots-per-wave shapes; nothing outside [a, a + n) is
+    # written
+    df, torch, dev = env
+    host = fold_inputs.slots("varied", W, n, 900 + W + n, spread=3.0)
+    want = oracle.fold_stacked(host)
+    for phase in (0, 3):
+        _say("case: fused round W=%d n=%d phase %d" % (W, n, phase))
+        allocs = [torch.full((n + 8,), float("nan"), dtype=torch.float32, device=dev) for _ in range(W)]
+        arenas = [a[phase:phase + n] for a in allocs]
+        for r in range(W):
+            arenas[r].copy_(torch.from_numpy(host[r]))
+        df.loopback_round(arenas, fused=True)
+        for r in range(W):
+            full = _host(torch, allocs[r])
+            _assert_bits(full[phase:phase + n], want, "W=%d n=%d phase %d arena %d" % (W, n, phase, r))
+            assert np.isnan(full[:phase]).all() and np.isnan(full[phase + n:]).all()
 
 
 def test_loopback_round_twice_doubles(env):
@@ -153,12 +176,13 @@ def test_loopback_round_twice_doubles(env):
     W, n = 4, 65_537
     host = fold_inputs.slots("vecf", W, n, 77)
     s = oracle.fold_stacked(host)
-    arenas = [_placed(torch, dev, host[r], 0) for r in range(W)]
-    df.loopback_round(arenas, direct=True)
-    df.loopback_round(arenas, direct=True)
     want = oracle.fold([s] * W)
-    for r in range(W):
-        _assert_bits(_host(torch, arenas[r]), want, "second round arena %d" % r)
+    for mode in ("direct", "fused"):
+        arenas = [_placed(torch, dev, host[r], 0) for r in range(W)]
+        df.loopback_round(arenas, direct=(mode == "direct"), fused=(mode == "fused"))
+        df.loopback_round(arenas, direct=(mode == "direct"), fused=(mode == "fused"))
+        for r in range(W):
+            _assert_bits(_host(torch, arenas[r]), want, "%s second round arena %d" % (mode, r))
 
 
 def test_loopback_round_one_rank_is_a_no_op(env):
