@@ -656,15 +656,15 @@ rows_kernel_t pick_rows(int32_t w, int spw)
     case 3: return k_fold_rows<3, 1, SCALED>;
     case 4: return k_fold_rows<4, 1, SCALED>;
     case 5: return k_fold_rows<5, 1, SCALED>;
-    case 6: return k_fold_rows<6, 1, SCALED>;
+    case 6: return spw == 2 ? k_fold_rows<6, 2, SCALED> : k_fold_rows<6, 1, SCALED>;
     case 7: return k_fold_rows<7, 1, SCALED>;
     case 8: return spw == 2 ? k_fold_rows<8, 2, SCALED> : k_fold_rows<8, 1, SCALED>;
     case 9: return k_fold_rows<9, 1, SCALED>;
-    case 10: return k_fold_rows<10, 1, SCALED>;
+    case 10: return spw == 2 ? k_fold_rows<10, 2, SCALED> : k_fold_rows<10, 1, SCALED>;
     case 11: return k_fold_rows<11, 1, SCALED>;
-    case 12: return k_fold_rows<12, 1, SCALED>;
+    case 12: return spw == 2 ? k_fold_rows<12, 2, SCALED> : k_fold_rows<12, 1, SCALED>;
     case 13: return k_fold_rows<13, 1, SCALED>;
-    case 14: return k_fold_rows<14, 1, SCALED>;
+    case 14: return spw == 2 ? k_fold_rows<14, 2, SCALED> : k_fold_rows<14, 1, SCALED>;
     case 15: return k_fold_rows<15, 1, SCALED>;
     default: return spw == 2 ? k_fold_rows<16, 2, SCALED> : k_fold_rows<16, 1, SCALED>;
     }
@@ -679,15 +679,15 @@ rows_all_kernel_t pick_rows_all(int32_t w, int spw)
     case 3: return k_fold_rows_all<3, 1>;
     case 4: return k_fold_rows_all<4, 1>;
     case 5: return k_fold_rows_all<5, 1>;
-    case 6: return k_fold_rows_all<6, 1>;
+    case 6: return spw == 2 ? k_fold_rows_all<6, 2> : k_fold_rows_all<6, 1>;
     case 7: return k_fold_rows_all<7, 1>;
     case 8: return spw == 2 ? k_fold_rows_all<8, 2> : k_fold_rows_all<8, 1>;
     case 9: return k_fold_rows_all<9, 1>;
-    case 10: return k_fold_rows_all<10, 1>;
+    case 10: return spw == 2 ? k_fold_rows_all<10, 2> : k_fold_rows_all<10, 1>;
     case 11: return k_fold_rows_all<11, 1>;
-    case 12: return k_fold_rows_all<12, 1>;
+    case 12: return spw == 2 ? k_fold_rows_all<12, 2> : k_fold_rows_all<12, 1>;
     case 13: return k_fold_rows_all<13, 1>;
-    case 14: return k_fold_rows_all<14, 1>;
+    case 14: return spw == 2 ? k_fold_rows_all<14, 2> : k_fold_rows_all<14, 1>;
     case 15: return k_fold_rows_all<15, 1>;
     default: return spw == 2 ? k_fold_rows_all<16, 2> : k_fold_rows_all<16, 1>;
     }

@@ -36,9 +36,9 @@ constexpr int rows_kib_per_wave(int w)
     return w <= 2 ? 8 : (w + 3) / 4;
 }
 
-// Eight- and sixteen-slot folds have a second shape, in which each wave
-// streams 1 KiB of several slots per tile (SPW slots per wave; the plan picks
-// it, see rows_slots_per_wave).  Measured on MI355X:
+// Even widths from six to sixteen have a second shape, in which each wave
+// streams 1 KiB of two slots per tile (SPW = 2; the plan picks it, see
+// rows_slots_per_wave).  Measured on MI355X:
 //  * W = 8, two slots per wave (four waves): 1.5-12% faster wherever the slot
 //    length is not a multiple of 2^24 floats, 0.8-1.4% slower where it is
 //    (2^24, 2^25, 2^26), whose 64 MiB-aligned runs the one-slot shape suits;
@@ -47,7 +47,12 @@ constexpr int rows_kib_per_wave(int w)
 //    the stacked fold at six lengths, 1.4-6% on separate slots, 2-16% on the
 //    fused round, and up to 30% faster than one slot per wave (16 waves x
 //    4 KiB); with shifted slots one slot per wave stays best (several slots
-//    per wave lose 3-12%).
+//    per wave lose 3-12%);
+//  * W = 6, 10, 12, 14, every slot at out's phase: 3.7-15% faster than one
+//    slot per wave at slot lengths of 6e6 to 1.26e7 (arenas beyond the
+//    memory-side cache); with shifted slots it loses up to 5% at W = 10 and
+//    12, so shifted arenas keep one slot per wave.  W = 4 keeps one slot per
+//    wave: two lose 6-8% at 2^24 and 1e8.
 // The shapes differ only in which wave loads which slot; every element's
 // chain is the same.
 constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot lengths at this multiple

@@ -30,13 +30,13 @@ bool vector_legal(const Geometry &g)
 
 // Slots each wave of the row body streams: for eight slots two, unless they
 // are a stacked arena whose slot length is a multiple of kOneSlotAlign; for
-// sixteen slots two when every slot shares out's 16-byte phase; one
-// otherwise.
+// the other even widths from six to sixteen two when every slot shares out's
+// 16-byte phase; one otherwise.
 int rows_slots_per_wave(const Geometry &g)
 {
     if (g.w == 8)
         return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
-    if (g.w == 16)
+    if (g.w >= 6 && g.w <= kMaxRowsW && g.w % 2 == 0)
         return vector_legal(g) ? 2 : 1;
     return 1;
 }
