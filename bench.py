@@ -294,7 +294,7 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
             shape, str(scaled).lower(), p["grid"], p["block"], p["tile"])
     if p["path"] == df.PATH_ROWS:
         return "k_fold_rows<%d,%d,%s> grid=%d block=%d tile=%d" % (
-            W, 64 * W // p["block"], str(scaled).lower(), p["grid"], p["block"], p["tile"])
+            W, -(-W // (p["block"] // 64)), str(scaled).lower(), p["grid"], p["block"], p["tile"])
     body = "k_fold_vector" if p["path"] == df.PATH_VECTOR else "k_fold_scalar"
     ws = W if W in (1, 2, 4, 8, 16) else 0
     pol = 1 if p["policy"] == df.POLICY_STREAM else 0

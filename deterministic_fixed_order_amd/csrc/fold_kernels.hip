@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
 template <int W, int SPW> struct RowsShape {
     static constexpr int LPW = rows_kib_per_wave(W, SPW);  // KiB of each slot a wave streams per tile
     static constexpr int T = LPW * 64;                     // 16-byte groups per tile
-    static constexpr int WAVES = W / SPW;                  // wave q streams slots q*SPW .. q*SPW+SPW-1
+    static constexpr int WAVES = rows_waves(W, SPW);       // wave q streams slots q*SPW .. q*SPW+SPW-1 < W
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -273,7 +273,7 @@ __device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slot
 }
 
 template <int W, int SPW, bool SCALED>
-__global__ __launch_bounds__(W / SPW * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
+__global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
                                                             int64_t head, float inv_w)
 {
     constexpr int LPW = RowsShape<W, SPW>::LPW, T = RowsShape<W, SPW>::T;
@@ -295,6 +295,8 @@ __global__ __launch_bounds__(W / SPW * 64) void k_fold_rows(float *out, SlotTabl
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {  // this wave's slots
             const uint32_t r = wave * SPW + j;
+            if (r >= (uint32_t)W)
+                break;  // an odd width's last wave streams one slot
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
 #pragma unroll
             for (int u = 0; u < LPW; ++u)
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(W / SPW * 64) void k_fold_rows(float *out, SlotTabl
 // the head and tail elements are read, folded and written back by one thread
 // each.  Every byte of every slot is read once and written once.
 template <int W, int SPW>
-__global__ __launch_bounds__(W / SPW * 64) void k_fold_rows_all(SlotTable slots, int64_t len,
+__global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotTable slots, int64_t len,
                                                                 int64_t head)
 {
     constexpr int LPW = RowsShape<W, SPW>::LPW, T = RowsShape<W, SPW>::T;
@@ -359,6 +361,8 @@ __global__ __launch_bounds__(W / SPW * 64) void k_fold_rows_all(SlotTable slots,
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
             const uint32_t r = wave * SPW + j;
+            if (r >= (uint32_t)W)
+                break;  // an odd width's last wave streams one slot
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
 #pragma unroll
             for (int u = 0; u < LPW; ++u)
@@ -380,6 +384,8 @@ __global__ __launch_bounds__(W / SPW * 64) void k_fold_rows_all(SlotTable slots,
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
             const uint32_t r = wave * SPW + j;
+            if (r >= (uint32_t)W)
+                break;  // an odd width's last wave streams one slot
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {
@@ -655,17 +661,17 @@ rows_kernel_t pick_rows(int32_t w, int spw)
     case 2: return k_fold_rows<2, 1, SCALED>;
     case 3: return k_fold_rows<3, 1, SCALED>;
     case 4: return k_fold_rows<4, 1, SCALED>;
-    case 5: return k_fold_rows<5, 1, SCALED>;
+    case 5: return spw == 2 ? k_fold_rows<5, 2, SCALED> : k_fold_rows<5, 1, SCALED>;
     case 6: return spw == 2 ? k_fold_rows<6, 2, SCALED> : k_fold_rows<6, 1, SCALED>;
-    case 7: return k_fold_rows<7, 1, SCALED>;
+    case 7: return spw == 2 ? k_fold_rows<7, 2, SCALED> : k_fold_rows<7, 1, SCALED>;
     case 8: return spw == 2 ? k_fold_rows<8, 2, SCALED> : k_fold_rows<8, 1, SCALED>;
-    case 9: return k_fold_rows<9, 1, SCALED>;
+    case 9: return spw == 2 ? k_fold_rows<9, 2, SCALED> : k_fold_rows<9, 1, SCALED>;
     case 10: return spw == 2 ? k_fold_rows<10, 2, SCALED> : k_fold_rows<10, 1, SCALED>;
-    case 11: return k_fold_rows<11, 1, SCALED>;
+    case 11: return spw == 2 ? k_fold_rows<11, 2, SCALED> : k_fold_rows<11, 1, SCALED>;
     case 12: return spw == 2 ? k_fold_rows<12, 2, SCALED> : k_fold_rows<12, 1, SCALED>;
-    case 13: return k_fold_rows<13, 1, SCALED>;
+    case 13: return spw == 2 ? k_fold_rows<13, 2, SCALED> : k_fold_rows<13, 1, SCALED>;
     case 14: return spw == 2 ? k_fold_rows<14, 2, SCALED> : k_fold_rows<14, 1, SCALED>;
-    case 15: return k_fold_rows<15, 1, SCALED>;
+    case 15: return spw == 2 ? k_fold_rows<15, 2, SCALED> : k_fold_rows<15, 1, SCALED>;
     default: return spw == 2 ? k_fold_rows<16, 2, SCALED> : k_fold_rows<16, 1, SCALED>;
     }
 }
@@ -678,17 +684,17 @@ rows_all_kernel_t pick_rows_all(int32_t w, int spw)
     case 2: return k_fold_rows_all<2, 1>;
     case 3: return k_fold_rows_all<3, 1>;
     case 4: return k_fold_rows_all<4, 1>;
-    case 5: return k_fold_rows_all<5, 1>;
+    case 5: return spw == 2 ? k_fold_rows_all<5, 2> : k_fold_rows_all<5, 1>;
     case 6: return spw == 2 ? k_fold_rows_all<6, 2> : k_fold_rows_all<6, 1>;
-    case 7: return k_fold_rows_all<7, 1>;
+    case 7: return spw == 2 ? k_fold_rows_all<7, 2> : k_fold_rows_all<7, 1>;
     case 8: return spw == 2 ? k_fold_rows_all<8, 2> : k_fold_rows_all<8, 1>;
-    case 9: return k_fold_rows_all<9, 1>;
+    case 9: return spw == 2 ? k_fold_rows_all<9, 2> : k_fold_rows_all<9, 1>;
     case 10: return spw == 2 ? k_fold_rows_all<10, 2> : k_fold_rows_all<10, 1>;
-    case 11: return k_fold_rows_all<11, 1>;
+    case 11: return spw == 2 ? k_fold_rows_all<11, 2> : k_fold_rows_all<11, 1>;
     case 12: return spw == 2 ? k_fold_rows_all<12, 2> : k_fold_rows_all<12, 1>;
-    case 13: return k_fold_rows_all<13, 1>;
+    case 13: return spw == 2 ? k_fold_rows_all<13, 2> : k_fold_rows_all<13, 1>;
     case 14: return spw == 2 ? k_fold_rows_all<14, 2> : k_fold_rows_all<14, 1>;
-    case 15: return k_fold_rows_all<15, 1>;
+    case 15: return spw == 2 ? k_fold_rows_all<15, 2> : k_fold_rows_all<15, 1>;
     default: return spw == 2 ? k_fold_rows_all<16, 2> : k_fold_rows_all<16, 1>;
     }
 }
@@ -761,7 +767,7 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
         e = launch(k, grid, block, args, stream, done);
     } else if (p.path == DETFOLD_PATH_ROWS) {
-        const int spw = 64 * w / p.block;  // the plan's workgroup has one wave per spw slots
+        const int spw = rows_spw(w, p.block / 64);  // the plan's workgroup size names the shape
         rows_kernel_t k = scaled ? pick_rows<true>(w, spw) : pick_rows<false>(w, spw);
         SlotTable slots = {};
         for (int32_t r = 0; r < w; ++r)
@@ -788,7 +794,7 @@ int launch_rows_all(const Geometry &g, const detfold_plan &p, void *stream)
 {
     if (p.path != DETFOLD_PATH_ROWS || !g.has_table || g.w < 2 || g.w > kMaxRowsW)
         return DETFOLD_EINVAL;
-    const int spw = 64 * g.w / p.block;
+    const int spw = rows_spw(g.w, p.block / 64);
     rows_all_kernel_t k = pick_rows_all(g.w, spw);
     SlotTable slots = {};
     for (int32_t r = 0; r < g.w; ++r)

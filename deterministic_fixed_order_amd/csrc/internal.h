@@ -36,9 +36,9 @@ constexpr int rows_kib_per_wave(int w)
     return w <= 2 ? 8 : (w + 3) / 4;
 }
 
-// Even widths from six to sixteen have a second shape, in which each wave
-// streams 1 KiB of two slots per tile (SPW = 2; the plan picks it, see
-// rows_slots_per_wave).  Measured on MI355X:
+// Widths from five to sixteen have a second shape, in which each wave streams
+// 1 KiB of two slots per tile (SPW = 2; an odd width's last wave streams one;
+// the plan picks it, see rows_slots_per_wave).  Measured on MI355X:
 //  * W = 8, two slots per wave (four waves): 1.5-12% faster wherever the slot
 //    length is not a multiple of 2^24 floats, 0.8-1.4% slower where it is
 //    (2^24, 2^25, 2^26), whose 64 MiB-aligned runs the one-slot shape suits;
@@ -52,7 +52,9 @@ constexpr int rows_kib_per_wave(int w)
 //    slot per wave at slot lengths of 6e6 to 1.26e7 (arenas beyond the
 //    memory-side cache); with shifted slots it loses up to 5% at W = 10 and
 //    12, so shifted arenas keep one slot per wave.  W = 4 keeps one slot per
-//    wave: two lose 6-8% at 2^24 and 1e8.
+//    wave: two lose 6-8% at 2^24 and 1e8;
+//  * odd W = 5, 7, 9, 11 at out's phase: 4-21% faster; 13 and 15: 0.2-5.6%;
+//    W = 3 loses up to 3% and keeps one slot per wave.
 // The shapes differ only in which wave loads which slot; every element's
 // chain is the same.
 constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot lengths at this multiple
@@ -60,6 +62,13 @@ constexpr int rows_kib_per_wave(int w, int spw)
 {
     return spw == 1 ? rows_kib_per_wave(w) : 1;
 }
+
+// Waves of the row body: wave q streams slots q*spw .. q*spw+spw-1 that exist.
+constexpr int rows_waves(int w, int spw) { return (w + spw - 1) / spw; }
+
+// The slots per wave of a row-body workgroup of `waves` waves over w slots
+// (the inverse of rows_waves for the shapes the plan makes).
+constexpr int rows_spw(int w, int waves) { return (w + waves - 1) / waves; }
 
 // Memory policy of a launch.
 //  kStream  the bandwidth path: every input byte is read once, so loads carry

@@ -30,13 +30,13 @@ bool vector_legal(const Geometry &g)
 
 // Slots each wave of the row body streams: for eight slots two, unless they
 // are a stacked arena whose slot length is a multiple of kOneSlotAlign; for
-// the other even widths from six to sixteen two when every slot shares out's
-// 16-byte phase; one otherwise.
+// the other widths from five to sixteen two when every slot shares out's
+// 16-byte phase (an odd width's last wave streams one); one otherwise.
 int rows_slots_per_wave(const Geometry &g)
 {
     if (g.w == 8)
         return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
-    if (g.w >= 6 && g.w <= kMaxRowsW && g.w % 2 == 0)
+    if (g.w >= 5 && g.w <= kMaxRowsW)
         return vector_legal(g) ? 2 : 1;
     return 1;
 }
@@ -47,7 +47,7 @@ int rows_slots_per_wave(const Geometry &g)
 int rows_block(const Geometry &g)
 {
     if (g.w <= kMaxRowsW)
-        return 64 * g.w / rows_slots_per_wave(g);
+        return 64 * rows_waves(g.w, rows_slots_per_wave(g));
     return 64 * (vector_legal(g) ? kWideAlignedWaves : kWideWaves);
 }
 

@@ -44,11 +44,14 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
             fail("head + body + tail != len", W, len);
     }
     /* eight slots of a stacked arena: two slots per wave unless len is a multiple of 2^24;
-     * the other even widths from six to sixteen: two when every slot shares out's 16-byte phase */
+     * the other widths from five to sixteen: two when every slot shares out's 16-byte phase,
+     * an odd width's last wave streaming one */
     const int spw = W == 8 ? (len % ((int64_t)1 << 24) != 0 ? 2 : 1)
-                           : (W >= 6 && W <= 16 && W % 2 == 0 && coaligned) ? 2 : 1;
-    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * W / spw : coaligned ? 512 : 1024))
+                           : (W >= 5 && W <= 16 && coaligned) ? 2 : 1;
+    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * ((W + spw - 1) / spw) : coaligned ? 512 : 1024))
         fail("row body with the wrong workgroup size", W, len);
+    if (p->path == DETFOLD_PATH_ROWS && W <= 16 && spw == 2 && p->tile != 64)
+        fail("two-slot row body with the wrong tile", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W == 8 && p->tile != (spw == 2 ? 64 : 128))
         fail("eight-slot row body with the wrong tile", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W == 16 && p->tile != (spw == 2 ? 64 : 256))

@@ -151,14 +151,16 @@ def test_plan_eight_slot_shape_follows_the_slot_length(detfold_lib, n, spw):
     with pytest.raises(detfold_lib.DetfoldError):
         detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU,
                                     dict(path=detfold_lib.PATH_ROWS, block=bad, grid=0, unroll=0, policy=0))
-    # odd widths and four keep one slot per wave at any length; the other even
-    # widths take two when every slot shares out's phase (sixteen: see below)
-    for W in (4, 7, 13):
+    # three and four slots keep one slot per wave at any length; five to
+    # sixteen take two when every slot shares out's phase (an odd width's last
+    # wave streams one; sixteen: see below)
+    for W in (3, 4):
         q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), W, n, CU)
         assert q["block"] == 64 * W
-    for W in (6, 10, 12, 14):
+    for W in (5, 6, 7, 10, 12, 13, 14, 15):
         q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), W, n, CU)
-        assert (q["block"], q["tile"]) == ((32 * W, 64) if n % 4 == 0 else (64 * W, 64 * (-(-W // 4))))
+        two = (64 * (-(-W // 2)), 64)
+        assert (q["block"], q["tile"]) == (two if n % 4 == 0 else (64 * W, 64 * (-(-W // 4))))
 
 
 @pytest.mark.parametrize("W", [1, 17, 24])

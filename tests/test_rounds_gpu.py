@@ -105,11 +105,12 @@ def test_fold_slots_in_place_and_repeated_slots(env, W):
     _assert_bits(_host(torch, out), oracle.fold([host[0], host[1], host[0]]), "repeated slot")
 
 
-@pytest.mark.parametrize("W", [8, 16])
+@pytest.mark.parametrize("W", [5, 6, 7, 8, 9, 11, 12, 13, 14, 15, 16])
 @pytest.mark.parametrize("n", [5, 4096, 70001, 1 << 20])
-def test_fold_slots_co_aligned_takes_the_many_slots_per_wave_shape(env, W, n):
-    # every buffer at one 16-byte phase: the eight- and sixteen-slot row
-    # bodies stream several slots per wave; out of place and in place
+def test_co_aligned_folds_take_the_two_slots_per_wave_shape(env, W, n):
+    # every buffer at one 16-byte phase: the row body streams two slots per
+    # wave (an odd width's last wave one); fold_slots out of place and in
+    # place, and fold_ranks over a stacked arena at the same phase
     df, torch, dev = env
     host = fold_inputs.slots("varied", W, n, 700 + W + n, spread=3.0)
     want = oracle.fold([host[r] for r in range(W)])
@@ -121,6 +122,12 @@ def test_fold_slots_co_aligned_takes_the_many_slots_per_wave_shape(env, W, n):
         _assert_bits(_host(torch, out), want, "W=%d n=%d phase %d" % (W, n, phase))
         df.fold_slots(slots[W - 1], slots)  # in place on the last slot
         _assert_bits(_host(torch, slots[W - 1]), want, "W=%d n=%d phase %d in place" % (W, n, phase))
+        if n % 4 == 0:  # a stacked arena is co-aligned only when its slot length is
+            _say("case: co-aligned fold_ranks W=%d n=%d phase %d" % (W, n, phase))
+            stacked = _placed(torch, dev, host.reshape(-1), phase).view(W, n)
+            out2 = _placed(torch, dev, np.full(n, np.nan, np.float32), phase)
+            df.fold_ranks(out2, stacked)
+            _assert_bits(_host(torch, out2), want, "stacked W=%d n=%d phase %d" % (W, n, phase))
 
 
 # --------------------------------------------------------------------------
@@ -147,7 +154,7 @@ def test_loopback_round_every_arena_holds_the_fold(env, W, n):
             _assert_bits(_host(torch, arenas[r]), want, "W=%d n=%d %s arena %d" % (W, n, mode, r))
 
 
-@pytest.mark.parametrize("W", [2, 4, 8, 16])
+@pytest.mark.parametrize("W", [2, 4, 5, 7, 8, 13, 16])
 @pytest.mark.parametrize("n", [1, 6, 4096, 70_001, 1 << 20])
 def test_fused_round_on_co_aligned_arenas(env, W, n):
     # every arena at one 16-byte phase: the eight- and sixteen-arena rounds
