@@ -230,14 +230,13 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
     fold_tiles<WS, U, float, SCALED, POL>(out, s0, s1, stride, w, len, inv_w);
 }
 
-// LDS row-transpose body (2 <= W <= 16).  One workgroup of W/SPW waves folds
-// a tile of T 16-byte groups of `out`: wave q streams the tile's bytes of its
-// SPW slots q*SPW .. q*SPW+SPW-1 -- LPW consecutive KiB of each, one
-// contiguous run per slot -- straight into LDS rows (buffer loads with the lds
-// bit, no register staging); after a barrier every thread folds whole groups
-// from the W rows, in ascending row order, and stores them.  SPW is 1 except
-// for the eight- and sixteen-slot shapes that stream several slots per wave
-// (see rows_kib_per_wave).
+// LDS row-transpose body (2 <= W <= 16).  One workgroup of ceil(W/SPW) waves
+// folds a tile of T 16-byte groups of `out`: wave q streams the tile's bytes
+// of its slots q*SPW .. q*SPW+SPW-1 that exist -- LPW consecutive KiB of each,
+// one contiguous run per slot -- straight into LDS rows (buffer loads with the
+// lds bit, no register staging); after a barrier every thread folds whole
+// groups from the W rows, in ascending row order, and stores them.  SPW is 1
+// or 2 (two slots of 1 KiB per wave; the plan's rows_slots_per_wave picks).
 // Streaming whole runs of a slot keeps each wave on few runs of HBM rows; the
 // direct body instead has every wave touch W runs 1 KiB at a time, which
 // measured 3-8% slower on MI355X.
