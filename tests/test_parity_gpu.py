@@ -486,6 +486,37 @@ def test_graph_replays_match_eager(env):
         _assert_bits(_host(eager), want, "eager between replays %d" % rep)
 
 
+def test_repeat_runs_are_bit_identical(env):
+    # run-to-run determinism: thirty folds of one order-sensitive arena,
+    # alternating between two streams and between the stacked, separate-slot
+    # and scaled entry points, each into its own output; every result must
+    # equal the first and the oracle, word for word
+    df, torch, dev = env
+    W, n = 8, (1 << 20) + 3
+    host = fold_inputs.slots("mixed", W, n, 4242)
+    want = oracle.fold_stacked(host)
+    stacked = _to_dev(torch, dev, host)
+    slots = [stacked[r] for r in range(W)]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream(dev))
+    outs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(30)]
+    for k, out in enumerate(outs):
+        st = streams[k % 2]
+        with torch.cuda.stream(st):
+            if k % 3 == 0:
+                df.fold_ranks(out, stacked)
+            elif k % 3 == 1:
+                df.fold_slots(out, slots)
+            else:
+                df.fold_ranks_scaled(out, stacked, 1.0)  # a multiply by one changes no bit
+    torch.cuda.synchronize()
+    first = _host(outs[0])
+    _assert_bits(first, want, "run 0")
+    for k, out in enumerate(outs[1:], 1):
+        _assert_bits(_host(out), first, "run %d" % k)
+
+
 def test_lengths_beyond_int32(env):
     """The pages' kernel took an i32 length; here len is 64-bit.  A W=2 fold of
     2^31 + 13 elements per slot (8 GiB each), checked on sampled outputs: 2^20
