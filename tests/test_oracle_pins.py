@@ -400,6 +400,19 @@ def test_pins_reject_scale_before_sum():
     assert failed
 
 
+def test_pins_reject_divide_by_the_width():
+    # the scale multiplies by the caller's inverse (one rounding of sum*inv);
+    # a mutant that divides by the width the inverse names (round(1/inv))
+    # agrees whenever inv is a power of two, so only the hand-derived golden
+    # case 2+2+1 times RN(1/3) tells the two apart
+    def scaled(S, inv):
+        return (oracle.fold_stacked(S) / np.float32(round(1.0 / float(inv)))).astype(np.float32)
+
+    with np.errstate(over="ignore", invalid="ignore"):
+        failed = _pin_failures(oracle.fold_stacked, scaled)
+    assert failed == ["golden:scaled3:40000000 40000000 3f800000"], failed
+
+
 def test_oracle_on_disjoint_ranges_equals_the_whole_fold():
     # the host oracle run on contiguous element ranges (as the threaded CPU
     # baseline does, one range per thread) gives the whole fold's bits: the

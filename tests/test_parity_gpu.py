@@ -21,6 +21,7 @@ Workloads (all inputs from ``fold_inputs``, seeded; none from the HIP path):
 Bar: 0 ULP -- every output word equal to the oracle's (NaN payloads are not
 pinned by the pages; only NaN-ness is compared where NaNs arise).
 """
+import os
 import sys
 
 import numpy as np
@@ -484,6 +485,57 @@ def test_graph_replays_match_eager(env):
         eager = torch.empty_like(out)
         df.fold_ranks(eager, stacked)  # eager work between replays
         _assert_bits(_host(eager), want, "eager between replays %d" % rep)
+
+
+def _golden_cases():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "binary32_fold_cases.txt")
+    cases = []
+    for line in open(path):
+        line = line.split(";")[0].strip()
+        if not line or line.startswith("#"):
+            continue
+        lhs, rhs = line.split("->")
+        toks = lhs.split()
+        inv = int(toks[-1][4:], 16) if toks[-1].startswith("inv=") else None
+        ops = [int(t, 16) for t in (toks[1:-1] if inv is not None else toks[1:])]
+        cases.append((toks[0], ops, inv, int(rhs.strip(), 16)))
+    return cases
+
+
+def test_golden_cases_on_the_device(env):
+    # every hand-derived IEEE 754 case of tests/golden, through the HIP path:
+    # each case's operands fill every column of a [W][1031] arena (so the row
+    # body's tiles, its head and its tail all see them) and every output word
+    # must be the case's expected word
+    df, torch, dev = env
+    n = 1031
+    cases = _golden_cases()
+    assert len(cases) > 40
+    for kind, ops, inv, want in cases:
+        what = "%s %s%s" % (kind, " ".join("%08x" % o for o in ops), " inv=%08x" % inv if inv else "")
+        col = np.array(ops, dtype=np.uint32).view(np.float32)
+        if kind == "into":
+            dst = _to_dev(torch, dev, np.full(n, col[0], np.float32))
+            stage = _to_dev(torch, dev, np.full(n, col[1], np.float32))
+            df.fold_into(dst, stage)
+            got = _host(dst)
+        else:
+            host = np.repeat(col.reshape(-1, 1), n, axis=1)
+            alloc = torch.empty(host.size + 1, dtype=torch.float32, device=dev)
+            for off in (0, 1):  # aligned, and shifted one element from out's phase
+                stacked = alloc[off:off + host.size].view(host.shape)
+                stacked.copy_(torch.from_numpy(host))
+                out = torch.empty(n, dtype=torch.float32, device=dev)
+                if kind.startswith("scaled"):
+                    df.fold_ranks_scaled(out, stacked, float(np.array([inv], np.uint32).view(np.float32)[0]))
+                else:
+                    df.fold_ranks(out, stacked)
+                got = _host(out)
+                bad = np.flatnonzero(got.view(np.uint32) != want)
+                assert bad.size == 0, "%s at +%d: got %08x want %08x" % (what, off, got.view(np.uint32)[bad[0]], want)
+            continue
+        bad = np.flatnonzero(got.view(np.uint32) != want)
+        assert bad.size == 0, "%s: got %08x want %08x" % (what, got.view(np.uint32)[bad[0]], want)
 
 
 def test_repeat_runs_are_bit_identical(env):
