@@ -132,3 +132,47 @@ def test_in_place_folds_on_random_shapes(env):
         df.fold_into(dst, stage)
         torch.cuda.synchronize()
         _assert_bits(dst.cpu().numpy(), oracle.fold_into(host[0], host[1]), what)
+
+
+def test_concurrent_folds_on_four_streams(env):
+    # forty folds of random shapes queued on four streams with no host
+    # synchronization between them (stacked, separate-slot and in-place
+    # entry points mixed), so that kernels of different shapes run side by
+    # side; every output must still equal its oracle fold
+    df, torch, dev = env
+    rng = np.random.default_rng(9400)
+    streams = [torch.cuda.Stream(device=dev) for _ in range(4)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream(dev))
+    jobs = []
+    for case in range(40):
+        kind = ("stacked", "slots", "into")[case % 3]
+        W = 2 if kind == "into" else int(rng.choice([2, 3, 5, 8, 12, 16, 20]))
+        if kind == "slots":
+            W = min(W, 16)
+        n = int(rng.integers(1, 200_000))
+        fam, host = _host_slots(rng, W, n, 70_000 + case)
+        off = int(rng.integers(0, 4))
+        st = streams[case % 4]
+        with torch.cuda.stream(st):
+            if kind == "stacked":
+                alloc = torch.empty(W * n + 4, dtype=torch.float32, device=dev)
+                stacked = alloc[off:off + W * n].view(W, n)
+                stacked.copy_(torch.from_numpy(host), non_blocking=False)
+                out = torch.empty(n, dtype=torch.float32, device=dev)
+                df.fold_ranks(out, stacked)
+                jobs.append((out, oracle.fold_stacked(host), "stacked W=%d n=%d +%d" % (W, n, off), alloc))
+            elif kind == "slots":
+                slots = [torch.from_numpy(host[r]).to(dev) for r in range(W)]
+                out = torch.empty(n, dtype=torch.float32, device=dev)
+                df.fold_slots(out, slots)
+                jobs.append((out, oracle.fold_stacked(host), "slots W=%d n=%d" % (W, n), slots))
+            else:
+                dst = torch.from_numpy(host[0]).to(dev)
+                stage = torch.from_numpy(host[1]).to(dev)
+                df.fold_into(dst, stage)
+                jobs.append((dst, oracle.fold_into(host[0], host[1]), "into n=%d" % n, stage))
+    _say("case: 40 folds on 4 streams queued")
+    torch.cuda.synchronize()
+    for out, want, what, _keep in jobs:
+        _assert_bits(out.cpu().numpy(), want, what)
