@@ -55,7 +55,7 @@ def build_library(out: str = LIB, extra: list[str] | None = None) -> str:
 
 
 def save_temps(outdir: str) -> None:
-    """Keep the gfx950 assembly of this build (for reading our own ISA)."""
+    """Keep the gfx950 assembly of the library's sources (for reading our own ISA)."""
     os.makedirs(outdir, exist_ok=True)
     cmd = [hipcc()] + flags() + ["-save-temps=obj", "-o", os.path.join(outdir, "libdetfold.so")] + SOURCES
     subprocess.run(cmd, check=True, cwd=outdir)
