@@ -271,6 +271,27 @@ __device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slot
     out[i] = acc;
 }
 
+// Wave `wave` streams the tile's bytes of its slots (wave*SPW .. wave*SPW+SPW-1
+// that exist) into their LDS rows: LPW KiB of each, through a descriptor based
+// at the slot's element e0 and limited to the tile's cnt groups.
+template <int W, int SPW, int LPW, int T>
+__device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const SlotTable &slots, int64_t e0,
+                                            int64_t cnt, uint32_t wave, uint32_t lane)
+{
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const uint32_t r = wave * SPW + j;
+        if (r >= (uint32_t)W)
+            break;  // an odd width's last wave streams one slot
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
+#pragma unroll
+        for (int u = 0; u < LPW; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
+                                                     (uint32_t)(u * 64 + lane) * 16u, 0, 0,
+                                                     Aux<kStream>::load);
+    }
+}
+
 template <int W, int SPW, bool SCALED>
 __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
                                                             int64_t head, float inv_w)
@@ -291,18 +312,7 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows(float *ou
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;  // first element of the tile; out + e0 is 16-byte aligned
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {  // this wave's slots
-            const uint32_t r = wave * SPW + j;
-            if (r >= (uint32_t)W)
-                break;  // an odd width's last wave streams one slot
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
-#pragma unroll
-            for (int u = 0; u < LPW; ++u)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
-                                                         (uint32_t)(u * 64 + lane) * 16u, 0, 0,
-                                                         Aux<kStream>::load);
-        }
+        stream_rows<W, SPW, LPW, T>(rows, slots, e0, cnt, wave, lane);
         __syncthreads();  // every row has landed
 
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + e0, (uint32_t)(cnt * 16));
@@ -357,18 +367,7 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            const uint32_t r = wave * SPW + j;
-            if (r >= (uint32_t)W)
-                break;  // an odd width's last wave streams one slot
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
-#pragma unroll
-            for (int u = 0; u < LPW; ++u)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
-                                                         (uint32_t)(u * 64 + lane) * 16u, 0, 0,
-                                                         Aux<kStream>::load);
-        }
+        stream_rows<W, SPW, LPW, T>(rows, slots, e0, cnt, wave, lane);
         __syncthreads();  // every row has landed
 
         for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += NT) {
