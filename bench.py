@@ -680,7 +680,7 @@ def _procs_join(rank, world, port):
     return dist
 
 
-def _procs_fold_main(rank, arenas, want, steps, warmup, port, results):
+def _procs_fold_main(rank, arenas, want, steps, warmup, fused_steps, port, results):
     """Rank `rank`: time its owner-shard fold over the mapped arenas, in turn."""
     import torch
     world = len(arenas)
@@ -701,6 +701,14 @@ def _procs_fold_main(rank, arenas, want, steps, warmup, port, results):
             results[rank] = timer.region(lambda: df.fold_slots(out, slots), steps) / steps
             same = torch.equal(out.view(torch.int32), want[start:start + length].view(torch.int32))
             results[world + rank] = 1.0 if same else 0.0
+        # every rank at once: the fused round over its own shard of all the arenas
+        # (the values grow by a factor W per round; bits are checked by the tests)
+        for _ in range(3):
+            df.loopback_round(slots, fused=True)
+        torch.cuda.synchronize()
+        dist.barrier()
+        results[2 * world + rank] = (timer.region(lambda: df.loopback_round(slots, fused=True), fused_steps)
+                                     / fused_steps)
         dist.barrier()
     finally:
         dist.destroy_process_group()
@@ -772,9 +780,14 @@ def bench_procs(args, torch, df, dev):
         moved.append((W + 1) * length * 4)
     torch.cuda.synchronize()
 
-    results = torch.zeros(2 * W, dtype=torch.float64).share_memory_()
+    steps_fused = min(args.steps, 20)  # the sums grow 4x per round: 4^(3 + 20) stays finite
+    local_fused = timer.region(lambda: df.loopback_round(arenas, fused=True), steps_fused) / steps_fused
+    for r in range(W):
+        arenas[r].copy_(torch.from_numpy(host[r]))
+    torch.cuda.synchronize()
+    results = torch.zeros(3 * W, dtype=torch.float64).share_memory_()
     log("procs: %d ranks fold their owner shards over mapped arenas" % W)
-    mp.spawn(_procs_fold_main, args=(arenas, want, args.steps, args.warmup, _free_port(), results),
+    mp.spawn(_procs_fold_main, args=(arenas, want, args.steps, args.warmup, steps_fused, _free_port(), results),
              nprocs=W, join=True)
     torch.cuda.ipc_collect()
     ranks = []
@@ -790,6 +803,16 @@ def bench_procs(args, torch, df, dev):
                                          row["bits_equal_unmapped"]))
     if not all(x["bits_equal_unmapped"] for x in ranks):
         raise RuntimeError("a rank's fold over mapped arenas differs from the unmapped fold")
+    fused_ms = max(float(results[2 * W + r]) for r in range(W))
+    fused = {"ms_per_round_slowest_rank": round(fused_ms, 4),
+             "GBps": round(2 * W * n * 4 / (fused_ms * 1e-3) / 1e9, 1),
+             "one_process_one_kernel_ms": round(local_fused, 4),
+             "one_process_GBps": round(2 * W * n * 4 / (local_fused * 1e-3) / 1e9, 1),
+             "note": "every rank at once runs the fused round over its own shard of all the mapped "
+                     "arenas; against one fused kernel over the whole arenas in one process"}
+    log("fused round, %d ranks at once over mapped arenas: %.4f ms per round (%.1f GB/s); one "
+        "process, one kernel: %.4f ms (%.1f GB/s)" % (W, fused_ms, fused["GBps"], local_fused,
+                                                       fused["one_process_GBps"]))
 
     m, calls = PROCS_SHOT_N, 500
     link = df.OneShotLink(m, device=dev)  # zeroes the counters and the words
@@ -822,7 +845,7 @@ def bench_procs(args, torch, df, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_sum, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": {"workload": WORKLOAD_NAMES["procs"], "W": W, "len": n},
-        "ranks": ranks,
+        "ranks": ranks, "fused_round_processes": fused,
         "one_shot_processes": {"n": m, "calls": calls, "us_per_call": per_call, "barrier_words": words},
     }
 

@@ -11,6 +11,10 @@ shard), then writes its reduced shard into the other ranks' arenas.  A CPU barri
 (gloo, host-side only) separates the phases.  Every arena must end equal to the
 oracle's fold of the original arenas, bit for bit.
 
+The fused test has every rank run the one-kernel fold-and-write-back round
+over its own shard of all the arenas at once, reading and writing the other
+ranks' arenas through the mapped handles.
+
 The one-shot test gives each of two processes its own rank's one-shot kernel
 (detfold_one_shot_rank); the staging buffers, barrier counters and refusal
 words are shared the same way, and the two kernels meet only through those
@@ -79,6 +83,54 @@ def test_processes_fold_through_shared_arenas(detfold_lib, world, n):
     print("case: %d processes, n=%d" % (world, n), flush=True)
     mp.spawn(_rank_main, args=(arenas, n, _free_port(), world), nprocs=world, join=True)
     torch.cuda.ipc_collect()  # release the handles the children held
+    for r in range(world):
+        got = arenas[r].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
+
+
+def _fused_rank_main(rank, arenas, n, port, world):
+    import sys
+    import torch
+    import torch.distributed as dist
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import deterministic_fixed_order_amd as df
+
+    os.environ["MASTER_ADDR"] = "127.0.0.1"
+    os.environ["MASTER_PORT"] = str(port)
+    dist.init_process_group("gloo", rank=rank, world_size=world)
+    try:
+        torch.cuda.set_device(0)
+        start, length = df.shard_plan(n, world)[rank]
+        dist.barrier()
+        if length:
+            # one kernel: my shard of every rank's arena, folded and written back to all of them
+            df.loopback_round([a[start:start + length] for a in arenas], fused=True)
+        torch.cuda.synchronize()
+        dist.barrier()
+    finally:
+        dist.destroy_process_group()
+
+
+@pytest.mark.parametrize("world,n", [(2, 1001), (4, 3), (4, 1 << 20)])
+def test_processes_fused_round_through_shared_arenas(detfold_lib, world, n):
+    # The one-sided shape of the sharded round: every rank runs the fused
+    # fold-and-write-back kernel over its own shard of all the arenas, reading
+    # and writing the other ranks' arenas through the mapped handles, all
+    # ranks at once (the shards are disjoint).  Every arena must end equal to
+    # the oracle's fold.
+    import torch
+    import torch.multiprocessing as mp
+
+    host = fold_inputs.slots("varied", world, n, 8900 + n, spread=2.0)
+    want = oracle.fold_stacked(host)
+    dev = torch.device("cuda:0")
+    arenas = [torch.from_numpy(host[r]).to(dev) for r in range(world)]
+    torch.cuda.synchronize()
+    print("case: fused round in %d processes, n=%d" % (world, n), flush=True)
+    mp.spawn(_fused_rank_main, args=(arenas, n, _free_port(), world), nprocs=world, join=True)
+    torch.cuda.ipc_collect()
     for r in range(world):
         got = arenas[r].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
