@@ -94,7 +94,9 @@ int fold_into(float *dst, const float *stage, int64_t n, void *stream);
  * finished sum (mamba-rs src/dist/reducer.rs module note: the kernel forms the
  * sum and the caller's 1/W scale follows it, exact for power-of-two W).  The
  * scale is the caller's: inv_w is not checked against W, and any value
- * (including non-powers of two) is applied as given.
+ * (including non-powers of two) is applied as given, with one rounding of
+ * sum * inv_w.  For W that is not a power of two this can differ from
+ * sum / W (5 * RN(1/3) rounds to 0x3fd55556, 5 / 3 to 0x3fd55555).
  * Arguments and errors as fold_ranks.
  */
 int fold_ranks_scaled(float *out, const float *stacked, int32_t W, int64_t len, float inv_w,
