@@ -248,9 +248,42 @@ def bench_fold(args, torch, df, dev):
         }
     if args.workload == "w8" and not args.no_latency:
         result["latency_16KiB"] = bench_join(args, torch, df, dev, timer)
+    if args.workload == "w16":
+        result["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step)
     return result
+
+
+def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
+    """The owner-shard form of the offset arena: each of the W owners' shards
+    is gathered once (untimed, device copies of the W slices) into a [W][l_p]
+    scratch, then the W shard folds run back to back per step into one output
+    at the owners' offsets, which must equal the whole-arena fold bit for bit.
+    Same algorithmic bytes as the whole fold, in W launches."""
+    import torch as _torch
+    shards = df.shard_plan(n, W)
+    scratch = [_torch.empty((W, l), dtype=_torch.float32, device=out.device) for _, l in shards]
+    for (s, l), sc in zip(shards, scratch):
+        sc.copy_(stacked[:, s:s + l])
+    out_sh = _torch.empty_like(out)
+
+    def step():
+        for (s, l), sc in zip(shards, scratch):
+            df.fold_ranks(out_sh[s:s + l], sc)
+    for _ in range(args.warmup):
+        step()
+    ms = timer.region(step, args.steps) / args.steps
+    _torch.cuda.synchronize()
+    same = bool(_torch.equal(out_sh.view(_torch.int32), out.view(_torch.int32)))
+    gbs = (W + 1) * n * 4 / (ms * 1e-3) / 1e9
+    log("owner shards: %d shard folds of about %d elements, %.4f ms per set (%.1f GB/s), bits equal "
+        "to the whole fold: %s" % (W, shards[0][1], ms, gbs, same))
+    if not same:
+        raise RuntimeError("the owner-shard folds differ from the whole-arena fold")
+    return {"shards": W, "shard_len_max": max(l for _, l in shards), "ms_per_set": round(ms, 5),
+            "GBps": round(gbs, 1), "bits_equal_whole_fold": same,
+            "note": "shards gathered once by device copies (untimed); the W shard folds timed back to back"}
 
 
 def bench_alternating(args, torch, df, dev, timer, stacked, out, bytes_per_step):
