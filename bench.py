@@ -248,7 +248,7 @@ def bench_fold(args, torch, df, dev):
         }
     if args.workload == "w8" and not args.no_latency:
         result["latency_16KiB"] = bench_join(args, torch, df, dev, timer)
-    if args.workload == "w16":
+    if args.workload == "w16" and args.owner_shards:
         result["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step)
@@ -894,6 +894,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-owner-shards", dest="owner_shards", action="store_false",
+                    help="skip the owner-shard folds of the w16 workload (profiling runs that "
+                         "summarize the whole fold's kernel)")
     ap.add_argument("--no-alternate", dest="alternate", action="store_false",
                     help="skip the two-arena control run")
     ap.add_argument("--sweep", action="store_true")
