@@ -122,12 +122,20 @@ def test_co_aligned_folds_take_the_two_slots_per_wave_shape(env, W, n):
         _assert_bits(_host(torch, out), want, "W=%d n=%d phase %d" % (W, n, phase))
         df.fold_slots(slots[W - 1], slots)  # in place on the last slot
         _assert_bits(_host(torch, slots[W - 1]), want, "W=%d n=%d phase %d in place" % (W, n, phase))
+        inv = np.float32(1.0 / W)
+        out3 = _placed(torch, dev, np.full(n, np.nan, np.float32), phase)
+        df.fold_slots_scaled(out3, slots[:W - 1] + [_placed(torch, dev, host[W - 1], phase)], float(inv))
+        _assert_bits(_host(torch, out3), oracle.fold_stacked_scaled(host, inv),
+                     "scaled W=%d n=%d phase %d" % (W, n, phase))
         if n % 4 == 0:  # a stacked arena is co-aligned only when its slot length is
             _say("case: co-aligned fold_ranks W=%d n=%d phase %d" % (W, n, phase))
             stacked = _placed(torch, dev, host.reshape(-1), phase).view(W, n)
             out2 = _placed(torch, dev, np.full(n, np.nan, np.float32), phase)
             df.fold_ranks(out2, stacked)
             _assert_bits(_host(torch, out2), want, "stacked W=%d n=%d phase %d" % (W, n, phase))
+            df.fold_ranks_scaled(out2, stacked, float(inv))
+            _assert_bits(_host(torch, out2), oracle.fold_stacked_scaled(host, inv),
+                         "stacked scaled W=%d n=%d phase %d" % (W, n, phase))
 
 
 # --------------------------------------------------------------------------
