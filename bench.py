@@ -320,7 +320,12 @@ def bench_alternating(args, torch, df, dev, timer, stacked, out, bytes_per_step)
 def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     """Name of the kernel instance the default launch uses (from the host plan)."""
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    p = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)
+    return plan_kernel_name(df, df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu), W, scaled)
+
+
+def plan_kernel_name(df, p, W, scaled) -> str:
+    """The kernel instance a host plan names: the row bodies by slots per wave
+    (W over the plan's waves, rounded up), the wide body by its pass shape."""
     if p["path"] == df.PATH_ROWS and W > 16:
         shape = "16,1,4" if p["block"] == 1024 else "8,2,1"  # waves, slots per wave, KiB
         return "k_fold_rows_wide<%s,%s> grid=%d block=%d tile=%d" % (

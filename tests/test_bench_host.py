@@ -1,5 +1,6 @@
 """Host-side pieces of bench.py: the code hash that ties the committed HBM
-counter record to the kernel source it was measured on."""
+counter record to the kernel source it was measured on, and the kernel names
+it reports from a host plan."""
 import bench
 
 
@@ -24,3 +25,17 @@ def test_counter_record_parses():
         assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
         assert rec["hbm_bytes_per_launch"] == int((rec["fetch_kib_per_launch"] * 2.0 +
                                                    rec["write_kib_per_launch"]) * 1024)
+
+
+def test_plan_kernel_names(detfold_lib):
+    df = detfold_lib
+    base, cu = 0x7F0000000000, 256
+    name = lambda out, st, W, n, scaled=False: bench.plan_kernel_name(
+        df, df.plan_fold_ranks(out, st, W, n, cu), W, scaled)
+    assert name(base, base + (1 << 34), 8, 1 << 24).startswith("k_fold_rows<8,1,false> grid=32768 block=512")
+    assert name(base, base + (1 << 34), 8, 10_000_000).startswith("k_fold_rows<8,2,false>")
+    assert name(base, base + (1 << 34), 7, 1 << 20).startswith("k_fold_rows<7,2,false> grid=4096 block=256")
+    assert name(base, base + (1 << 34) + 4, 7, 1 << 20).startswith("k_fold_rows<7,1,false> grid=2048 block=448")
+    assert name(base, base + (1 << 34), 4, 100_000_000, True).startswith("k_fold_rows<4,1,true>")
+    assert name(base, base + (1 << 34), 32, 1 << 20).startswith("k_fold_rows_wide<8,2,1,false>")
+    assert name(base, base + (1 << 34) + 4, 32, 1 << 20).startswith("k_fold_rows_wide<16,1,4,false>")
