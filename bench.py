@@ -220,10 +220,12 @@ def bench_fold(args, torch, df, dev):
                    "bytes_per_step": bytes_per_step, "parallelism": "single GPU"},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
     }
-    counters = read_counters() if name == "w8" else None
+    counters = read_counters()
     traffic = None
-    if counters:
+    if counters and name == "w8":
         traffic = counters.get("hbm_bytes_per_launch")
+    elif counters:
+        traffic = counters.get("other_workloads", {}).get(name, {}).get("hbm_bytes_per_launch")
     result["roofline"] = {
         "bound": "hbm",
         "achieved": round(gbs, 2),
