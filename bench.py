@@ -10,8 +10,13 @@ the timed region starts.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
 prints one JSON line: metric, value (GB/s of algorithmic bytes), the roofline
-of the fold kernel, the CPU oracle timed on the host as a reported baseline,
-and the 16 KiB in-place fold latency.  Other modes (not the headline):
+of the fold kernel (nominal and against the streaming ceiling measured on the
+same box), single launches after a cache scrub (event pair around the call and
+the kernel's own duration), the CPU oracle timed on the host as a reported
+baseline, the 16 KiB in-place fold latency, and two secondary fold workloads
+in the same line: W=4 x 1e8 mixed magnitudes scaled by 1/4, and W=16 x
+10,000,019 at base+1 element, whole and as 16 owner shards (each bit-checked
+against the oracle).  Other modes (not the headline):
 
     --workload {w8,w4,w16,w32}    other fold configurations, same JSON shape
     --workload {join,round,pair,procs}
@@ -167,20 +172,79 @@ def make_workload(name, torch, dev, want_host=False):
     return host, stacked, out, W, n, inv_w
 
 
-def bench_fold(args, torch, df, dev):
-    import numpy as np
+def fold_step(df, out, stacked, inv_w):
+    """One fold_ranks (or fold_ranks_scaled) call on the current stream."""
+    if inv_w is None:
+        return lambda: df.fold_ranks(out, stacked)
+    return lambda: df.fold_ranks_scaled(out, stacked, inv_w)
 
+
+def timing_events(torch, stream, count):
+    """`count` (start, stop) pairs of timing-enabled events, each recorded once
+    so that its device event exists before a dispatch records it."""
+    pairs = []
+    for _ in range(count):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return pairs
+
+
+def kernel_only_ms(torch, df, stream, out, stacked, inv_w, calls):
+    """Durations (ms) of `calls` back-to-back fold kernels, each timed by
+    events its own dispatch records (detfold_fold_ranks_timed)."""
+    pairs = timing_events(torch, stream, calls)
+    for a, b in pairs:
+        df.fold_ranks_timed(out, stacked, a, b, scaled=inv_w is not None,
+                            inv_w=inv_w if inv_w is not None else 1.0)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def oracle_check(host, inv_w, out):
+    """The whole GPU output against the CPU oracle, bit for bit."""
+    import numpy as np
+    import oracle
+    want = oracle.fold_stacked(host) if inv_w is None else \
+        oracle.fold_stacked_scaled(host, np.float32(inv_w))
+    got = out.cpu().numpy()
+    return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
+
+
+def traffic_for(name):
+    """HBM bytes per launch of workload `name` from the committed counter
+    record, if it was taken on the current library code; else None."""
+    counters = read_counters()
+    if not counters:
+        return None
+    if name == "w8":
+        return counters.get("hbm_bytes_per_launch")
+    return counters.get("other_workloads", {}).get(name, {}).get("hbm_bytes_per_launch")
+
+
+def roofline(gbs, ms, bytes_per_step, kernel, traffic, kernel_ms=None, attainable=None):
+    r = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+         "algorithmic_bytes_per_launch": bytes_per_step, "avg_launch_ms": round(ms, 6)}
+    if traffic:
+        r["traffic_over_algorithmic"] = round(traffic / bytes_per_step, 4)
+    if kernel_ms is not None:
+        r["kernel_only_avg_ms"] = round(kernel_ms, 6)
+    if attainable:
+        r["attainable_GBps"] = attainable
+        r["frac_of_attainable"] = round(gbs / attainable, 4)
+    return r
+
+
+def bench_fold(args, torch, df, dev):
     name = args.workload
     host, stacked, out, W, n, inv_w = make_workload(name, torch, dev)
     bytes_per_step = (W + 1) * n * 4
     stream = torch.cuda.current_stream(dev)
     timer = Timer(torch, stream)
-    if inv_w is None:
-        def step():
-            df.fold_ranks(out, stacked)
-    else:
-        def step():
-            df.fold_ranks_scaled(out, stacked, inv_w)
+    step = fold_step(df, out, stacked, inv_w)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -189,19 +253,15 @@ def bench_fold(args, torch, df, dev):
     ms_per_step = ms_total / args.steps
     gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log("timed region: %.3f ms per step, %.1f GB/s" % (ms_per_step, gbs))
+    kern = kernel_only_ms(torch, df, stream, out, stacked, inv_w, args.steps)
+    kern_avg = statistics.mean(kern)
+    log("kernel-only (dispatch-recorded events), %d back-to-back launches: average %.4f ms, "
+        "median %.4f ms" % (len(kern), kern_avg, statistics.median(kern)))
 
-    # per-launch event pairs, each call preceded by reading a 1 GiB scrub buffer,
-    # so the 256 MB last-level cache holds none of the operands (and no dirty
-    # lines to write back) when the fold starts
-    singles = []
-    if args.singles > 0:
-        scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        for i in range(args.singles):
-            scrub.sum()
-            singles.append(timer.region(step, 1))
-        del scrub
-        log("single launches after a cache scrub: median %.3f ms, best %.3f ms"
-            % (statistics.median(singles), min(singles)))
+    singles = bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step) \
+        if args.singles > 0 else None
+    ceiling = bench_ceiling(args, torch, dev, timer, stacked, out) if args.ceiling else None
+    attainable = ceiling["attainable_GBps"] if ceiling else None
 
     result = {
         "metric": METRIC,
@@ -220,41 +280,159 @@ def bench_fold(args, torch, df, dev):
                    "bytes_per_step": bytes_per_step, "parallelism": "single GPU"},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
     }
-    counters = read_counters()
-    traffic = None
-    if counters and name == "w8":
-        traffic = counters.get("hbm_bytes_per_launch")
-    elif counters:
-        traffic = counters.get("other_workloads", {}).get(name, {}).get("hbm_bytes_per_launch")
-    result["roofline"] = {
-        "bound": "hbm",
-        "achieved": round(gbs, 2),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(gbs / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
-        "kernel": kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
-        "algorithmic_bytes_per_launch": bytes_per_step,
-        "avg_launch_ms": round(ms_per_step, 6),
-    }
+    result["roofline"] = roofline(gbs, ms_per_step, bytes_per_step,
+                                  kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
+                                  traffic_for(name), kern_avg, attainable)
     if args.alternate and inv_w is None:
         result["alternating_arenas"] = bench_alternating(args, torch, df, dev, timer, stacked, out,
                                                          bytes_per_step)
     if singles:
-        result["scrubbed_single_launch"] = {
-            "median_ms": round(statistics.median(singles), 6),
-            "best_ms": round(min(singles), 6),
-            "median_GBps": round(bytes_per_step / (statistics.median(singles) * 1e-3) / 1e9, 2),
-            "calls": len(singles),
-            "note": "event pair per call, 1 GiB scrub read before each",
-        }
+        result["scrubbed_single_launch"] = singles
+    if ceiling:
+        result["streaming_ceiling"] = ceiling
+    result["device"] = device_info(torch, dev)
     if args.workload == "w8" and not args.no_latency:
         result["latency_16KiB"] = bench_join(args, torch, df, dev, timer)
     if args.workload == "w16" and args.owner_shards:
         result["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step)
+    else:
+        result["bit_exact_vs_oracle"] = oracle_check(host, inv_w, out)
+    if args.workload == "w8" and args.secondary:
+        del host, stacked, out
+        torch.cuda.empty_cache()
+        result["secondary"] = {w: bench_secondary(args, torch, df, dev, w) for w in ("w4", "w16")}
     return result
+
+
+def bench_secondary(args, torch, df, dev, name):
+    """Another fold workload in the same run: back-to-back throughput, the
+    kernel's own duration, the roofline against the nominal peak, the HBM
+    traffic record, and the whole output checked against the CPU oracle bit
+    for bit; for the W=16 arena also its 16 owner shards."""
+    host, stacked, out, W, n, inv_w = make_workload(name, torch, dev)
+    bytes_per_step = (W + 1) * n * 4
+    stream = torch.cuda.current_stream(dev)
+    timer = Timer(torch, stream)
+    step = fold_step(df, out, stacked, inv_w)
+    for _ in range(args.warmup):
+        step()
+    ms = timer.region(step, args.steps) / args.steps
+    gbs = bytes_per_step / (ms * 1e-3) / 1e9
+    kern = kernel_only_ms(torch, df, stream, out, stacked, inv_w, args.steps)
+    exact = oracle_check(host, inv_w, out)
+    log("%s: %.4f ms per step, %.1f GB/s (%.1f%% of peak); kernel-only average %.4f ms; bit-exact vs "
+        "the oracle: %s" % (name, ms, gbs, 100 * gbs / HBM_PEAK_GBS, statistics.mean(kern), exact))
+    if not exact:
+        raise RuntimeError("%s: the GPU fold differs from the oracle" % name)
+    res = {"workload": WORKLOAD_NAMES[name], "W": W, "len": n, "bytes_per_step": bytes_per_step,
+           "steps": args.steps, "ms_per_step": round(ms, 6), "GBps": round(gbs, 2),
+           "kernel_only_median_ms": round(statistics.median(kern), 6),
+           "roofline": roofline(gbs, ms, bytes_per_step,
+                                kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
+                                traffic_for(name), statistics.mean(kern)),
+           "bit_exact_vs_oracle": exact}
+    if name == "w16" and args.owner_shards:
+        res["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
+    del host, stacked, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step):
+    """Single launches, each after writing a 1 GiB scrub buffer (more than
+    four times the 256 MB memory-side cache, so it holds none of the fold's
+    operands when the call starts).  Every call is timed twice at once: by an
+    event pair recorded around it on the stream (launch and event latency
+    included), and by the start/stop events its own dispatch records (the
+    kernel alone)."""
+    stream = timer.stream
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    pairs = timing_events(torch, stream, args.singles)
+    outer, inner = [], []
+    for i, (a, b) in enumerate(pairs):
+        scrub.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        df.fold_ranks_timed(out, stacked, a, b, scaled=inv_w is not None,
+                            inv_w=inv_w if inv_w is not None else 1.0)
+        e1.record(stream)
+        e1.synchronize()
+        outer.append(e0.elapsed_time(e1))
+        inner.append(a.elapsed_time(b))
+    del scrub
+    torch.cuda.synchronize()
+    med_o, med_i = statistics.median(outer), statistics.median(inner)
+    gb = lambda ms: round(bytes_per_step / (ms * 1e-3) / 1e9, 2)
+    log("single launches after a 1 GiB scrub write: event pair around the call median %.4f ms "
+        "(%.1f GB/s), kernel alone median %.4f ms (%.1f GB/s)" % (med_o, gb(med_o), med_i, gb(med_i)))
+    return {"calls": len(outer), "scrub": "1 GiB written (fill) before each call",
+            "kernel_only_median_ms": round(med_i, 6), "kernel_only_best_ms": round(min(inner), 6),
+            "kernel_only_median_GBps": gb(med_i),
+            "kernel_only_frac": round(gb(med_i) / HBM_PEAK_GBS, 4),
+            "event_pair_median_ms": round(med_o, 6), "event_pair_best_ms": round(min(outer), 6),
+            "event_pair_median_GBps": gb(med_o),
+            "note": "kernel_only: start/stop events recorded by the fold's own dispatch; event_pair: "
+                    "events recorded on the stream before and after the call"}
+
+
+def bench_ceiling(args, torch, dev, timer, stacked, out):
+    """What plain streaming reaches on this machine with library kernels: torch
+    reductions over the slot axis of the same arena (the fold's byte mix, W
+    reads to one write: amax carries no additions, sum other ones), a device
+    copy of the whole arena (1:1), a fill of it (writes only) and a sum of it
+    to one value (reads only).  Each rate counts the bytes the operation must
+    move, over back-to-back calls timed with events.  attainable_GBps is the
+    best of them."""
+    W, n = stacked.shape
+    arena = W * n * 4
+    tmp = torch.empty_like(out)
+    scratch = torch.empty_like(stacked)
+    probes = {
+        "amax_over_slots": (lambda: torch.amax(stacked, dim=0, out=tmp), arena + n * 4),
+        "sum_over_slots": (lambda: torch.sum(stacked, dim=0, out=tmp), arena + n * 4),
+        "copy_arena": (lambda: scratch.copy_(stacked), 2 * arena),
+        "fill_arena": (lambda: scratch.fill_(1.0), arena),
+        "sum_arena_to_scalar": (lambda: stacked.sum(), arena),
+    }
+    reps = max(5, min(args.steps, 50))
+    res = {}
+    for key, (fn, moved) in probes.items():
+        for _ in range(3):
+            fn()
+        ms = timer.region(fn, reps) / reps
+        res[key] = {"ms": round(ms, 6), "bytes": moved, "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+        log("ceiling probe %-20s %.4f ms, %.1f GB/s" % (key, ms, res[key]["GBps"]))
+    del tmp, scratch
+    torch.cuda.empty_cache()
+    best = max(res, key=lambda k: res[k]["GBps"])
+    return {"probes": res, "attainable_GBps": res[best]["GBps"], "best_probe": best,
+            "note": "library streaming kernels on the headline arena (torch reductions, copy, fill), "
+                    "back-to-back, bytes each operation must move"}
+
+
+def device_info(torch, dev):
+    """What the device reports: CU count, peak memory clock and bus width (HIP
+    device attributes), and the HBM rate those imply (two transfers per clock)."""
+    import ctypes
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count, "total_memory_bytes": props.total_memory}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        attrs = {"memory_clock_khz": 60, "memory_bus_width_bits": 59, "core_clock_khz": 5}
+        for key, attr in attrs.items():  # hipDeviceAttribute_t values of hip_runtime_api.h
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev.index or 0) == 0:
+                info[key] = v.value
+        if info.get("memory_clock_khz") and info.get("memory_bus_width_bits"):
+            info["hbm_GBps_from_clock_and_width"] = round(
+                2 * info["memory_clock_khz"] * 1e3 * info["memory_bus_width_bits"] / 8 / 1e9, 1)
+    except OSError:
+        pass
+    return info
 
 
 def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
@@ -906,6 +1084,10 @@ def main(argv=None) -> int:
                          "summarize the whole fold's kernel)")
     ap.add_argument("--no-alternate", dest="alternate", action="store_false",
                     help="skip the two-arena control run")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="skip the library streaming probes (the attainable ceiling)")
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="skip the W=4 and W=16 workloads after the headline")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)

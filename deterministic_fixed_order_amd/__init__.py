@@ -33,7 +33,7 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 6
+ABI_VERSION = 7
 ONE_SHOT_BLOCKS = 64
 ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
 BARRIER_ENTRY_EXPIRED, BARRIER_EXIT_EXPIRED = 40043, 40044
@@ -45,7 +45,7 @@ EXPORTS = (
     "detfold_fold_ranks_ex", "fold_slots", "fold_slots_scaled", "detfold_loopback_round",
     "detfold_pair_link_init", "detfold_pair_all_reduce", "detfold_pair_broadcast",
     "detfold_pair_all_gather", "detfold_one_shot_init", "detfold_one_shot_all_reduce",
-    "detfold_one_shot_rank",
+    "detfold_one_shot_rank", "detfold_fold_ranks_timed",
 )
 
 
@@ -100,6 +100,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fold_ranks_scaled.argtypes = [f32p, f32p, i32, i64, ctypes.c_float, vp]
     lib.detfold_fold_ranks_ex.argtypes = [f32p, f32p, i32, i64, i32, ctypes.c_float,
                                           ctypes.POINTER(Launch), vp]
+    lib.detfold_fold_ranks_timed.argtypes = [f32p, f32p, i32, i64, i32, ctypes.c_float,
+                                             ctypes.POINTER(Launch), vp, vp, vp]
     lib.detfold_strerror.argtypes = [ctypes.c_int]
     lib.detfold_strerror.restype = ctypes.c_char_p
     lib.detfold_abi_version.argtypes = []
@@ -219,6 +221,26 @@ def fold_ranks_ex(out, stacked, *, scaled: bool = False, inv_w: float = 1.0, pat
     _check(load().detfold_fold_ranks_ex(out.data_ptr(), stacked.data_ptr(), W, n, int(scaled),
                                         float(inv_w), ctypes.byref(cfg),
                                         _stream_handle(out, stream)), "detfold_fold_ranks_ex")
+
+
+def fold_ranks_timed(out, stacked, start, stop, *, scaled: bool = False, inv_w: float = 1.0,
+                     launch: Optional[dict] = None, stream=None) -> None:
+    """``fold_ranks`` / ``fold_ranks_scaled`` whose kernel dispatch records the
+    timing-enabled ``torch.cuda.Event`` objects ``start`` and ``stop`` itself
+    (measurement only): ``start.elapsed_time(stop)`` is the kernel's own
+    duration.  Both events must have been recorded once before, so that their
+    device events exist."""
+    W, n = _stacked_shape(out, stacked)
+    handles = []
+    for e, nm in ((start, "start"), (stop, "stop")):
+        h = int(e.cuda_event) if e is not None else 0
+        if e is not None and not h:
+            raise ValueError("%s has no device event yet; record it once first" % nm)
+        handles.append(h or None)
+    cfg = ctypes.byref(Launch(**launch)) if launch else None
+    _check(load().detfold_fold_ranks_timed(out.data_ptr(), stacked.data_ptr(), W, n, int(scaled),
+                                           float(inv_w), cfg, _stream_handle(out, stream),
+                                           handles[0], handles[1]), "detfold_fold_ranks_timed")
 
 
 def _ptr_array(tensors):

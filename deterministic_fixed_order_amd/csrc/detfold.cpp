@@ -43,7 +43,7 @@ int current_cu_count(int32_t *cu)
 }
 
 int run_ranks(float *out, const float *stacked, int32_t W, int64_t len, bool scaled, float inv_w,
-              const detfold_launch *ovr, void *stream)
+              const detfold_launch *ovr, void *stream, void *begin = nullptr, void *done = nullptr)
 {
     int rc = check_ranks_args(out, stacked, W, len);
     if (rc == DETFOLD_OK)
@@ -59,7 +59,7 @@ int run_ranks(float *out, const float *stacked, int32_t W, int64_t len, bool sca
     detfold_plan p;
     if ((rc = make_plan(g, cu, ovr, DETFOLD_POLICY_STREAM, &p)) != DETFOLD_OK)
         return rc;
-    return launch_plan(g, p, scaled, inv_w, static_cast<hipStream_t>(stream));
+    return launch_plan(g, p, scaled, inv_w, static_cast<hipStream_t>(stream), done, begin);
 }
 
 // Launch the fold of separate slots (arguments already checked, len > 0).
@@ -278,6 +278,13 @@ int detfold_fold_ranks_ex(float *out, const float *stacked, int32_t W, int64_t l
                           float inv_w, const detfold_launch *launch, void *stream)
 {
     return run_ranks(out, stacked, W, len, scaled != 0, inv_w, launch, stream);
+}
+
+int detfold_fold_ranks_timed(float *out, const float *stacked, int32_t W, int64_t len, int32_t scaled,
+                             float inv_w, const detfold_launch *launch, void *stream, void *start,
+                             void *stop)
+{
+    return run_ranks(out, stacked, W, len, scaled != 0, inv_w, launch, stream, start, stop);
 }
 
 int fold_into(float *dst, const float *stage, int64_t n, void *stream)

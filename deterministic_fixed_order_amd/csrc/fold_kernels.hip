@@ -724,12 +724,13 @@ scalar_kernel_t pick_scalar(int32_t w, int unroll, int policy)
 }
 
 // Launch a kernel; with `done`, the event is recorded by the dispatch itself
-// when the kernel completes (cheaper than a separate event record).
+// when the kernel completes (cheaper than a separate event record), and with
+// `begin` when it starts, so the pair times the kernel alone.
 hipError_t launch(const void *k, dim3 grid, dim3 block, void **args, hipStream_t stream,
-                  hipEvent_t done)
+                  hipEvent_t done, hipEvent_t begin = nullptr)
 {
-    if (done)
-        return hipExtLaunchKernel(k, grid, block, args, 0, stream, nullptr, done, 0);
+    if (done || begin)
+        return hipExtLaunchKernel(k, grid, block, args, 0, stream, begin, done, 0);
     return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 
@@ -740,10 +741,11 @@ hipError_t launch(const void *k, dim3 grid, dim3 block, void **args, hipStream_t
 // and enqueue it on the caller's stream.
 
 int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv_w, void *stream_,
-                void *done_)
+                void *done_, void *begin_)
 {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     hipEvent_t done = static_cast<hipEvent_t>(done_);
+    hipEvent_t begin = static_cast<hipEvent_t>(begin_);
     float *out = reinterpret_cast<float *>(g.out);
     const float *s0 = reinterpret_cast<const float *>(g.s0);
     const float *s1 = reinterpret_cast<const float *>(g.s1);
@@ -763,7 +765,7 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
                                 : (scaled ? (const void *)k_fold_rows_wide<kWideWaves, 1, kWideKiB, true>
                                           : (const void *)k_fold_rows_wide<kWideWaves, 1, kWideKiB, false>);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
-        e = launch(k, grid, block, args, stream, done);
+        e = launch(k, grid, block, args, stream, done, begin);
     } else if (p.path == DETFOLD_PATH_ROWS) {
         const int spw = rows_spw(w, p.block / 64);  // the plan's workgroup size names the shape
         rows_kernel_t k = scaled ? pick_rows<true>(w, spw) : pick_rows<false>(w, spw);
@@ -771,17 +773,17 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
         for (int32_t r = 0; r < w; ++r)
             slots.p[r] = reinterpret_cast<const float *>(g.slot(r));
         void *args[] = {&out, &slots, &len, &head, &inv_w};
-        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
+        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done, begin);
     } else if (p.path == DETFOLD_PATH_VECTOR) {
         vector_kernel_t k = scaled ? pick_vector<true>(w, p.unroll, policy)
                                    : pick_vector<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
-        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
+        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done, begin);
     } else {
         scalar_kernel_t k = scaled ? pick_scalar<true>(w, p.unroll, policy)
                                    : pick_scalar<false>(w, p.unroll, policy);
         void *args[] = {&out, &s0, &s1, &stride, &w, &len, &inv_w};
-        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done);
+        e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done, begin);
     }
     return e == hipSuccess ? DETFOLD_OK : DETFOLD_ELAUNCH;
 }

@@ -165,9 +165,10 @@ OneShotArgs one_shot_args(const detfold_one_shot_link *k, int32_t rank0, int nra
 
 // --- fold_kernels.hip: launches (hipStream_t and hipEvent_t passed as void*) -
 // With `done`, the event is recorded by the dispatch itself when the kernel
-// completes.  Each returns DETFOLD_OK or DETFOLD_ELAUNCH.
+// completes, with `begin` when it starts.  Each returns DETFOLD_OK or
+// DETFOLD_ELAUNCH.
 int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv_w, void *stream,
-                void *done = nullptr);
+                void *done = nullptr, void *begin = nullptr);
 int launch_copy(float *const *dsts, int ndst, const float *src, int64_t len, int32_t cu,
                 void *stream, void *done = nullptr);
 // Every slot of a table geometry becomes the fold of all (the fused round);

@@ -298,7 +298,7 @@ int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 6
+#define DETFOLD_ABI_VERSION 7
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -394,6 +394,27 @@ int detfold_plan_fold_into(uintptr_t dst, uintptr_t stage, int64_t n, int32_t cu
  */
 int detfold_fold_ranks_ex(float *out, const float *stacked, int32_t W, int64_t len, int32_t scaled,
                           float inv_w, const detfold_launch *launch, void *stream);
+
+/*
+ * detfold_fold_ranks_timed -- detfold_fold_ranks_ex whose kernel dispatch
+ * itself records two caller-owned events: `start` when the fold kernel begins
+ * and `stop` when it has finished (hipExtLaunchKernel's start and stop
+ * events).  hipEventElapsedTime(start, stop) is then the kernel's own
+ * duration, free of the launch and event-record latency that an event pair
+ * recorded around the call includes (memra-engine src/bin/moe_tp2_repro.rs
+ * times with timing-enabled events and warns that a harness can end up timing
+ * itself rather than the device).  The fold is one kernel on every path, so
+ * the pair brackets all of its work.  For measurement; the bits are those of
+ * fold_ranks / fold_ranks_scaled.
+ *   start, stop  hipEvent_t of the current device created with timing
+ *                enabled, or NULL (that event is not recorded)
+ *   launch       may be NULL (the default plan)
+ * Errors: as detfold_fold_ranks_ex.  With len == 0 nothing is launched and
+ * neither event is recorded.
+ */
+int detfold_fold_ranks_timed(float *out, const float *stacked, int32_t W, int64_t len, int32_t scaled,
+                             float inv_w, const detfold_launch *launch, void *stream, void *start,
+                             void *stop);
 
 #ifdef __cplusplus
 }

@@ -11,11 +11,14 @@ FixedOrder-contract module note, the ``det_sum_ranks`` kernel source and
 ``reduce_sum_reference``; memra-engine ``tests/tp_ar_gpu.rs``:
 ``memra_tp_ar_fold``):
 
-* ``fold(slots)``            -- ``acc = s_0; acc = acc + s_r`` for r ascending,
-  each ``+`` one binary32 round-to-nearest-even addition, subnormals kept.
-* ``fold_scaled(slots, w)``  -- the same sum, then one binary32 multiply by
-  ``w`` (the caller's inverse world size).
-* ``fold_into(dst, stage)``  -- ``dst + stage`` elementwise.
+* ``fold(slots)``                       -- ``acc = s_0; acc = acc + s_r`` for r
+  ascending, each ``+`` one binary32 round-to-nearest-even addition,
+  subnormals kept.
+* ``fold_stacked(stacked)``             -- ``fold`` over the rows of a ``[W, len]``
+  array (row r = slot r).
+* ``fold_stacked_scaled(stacked, inv_w)`` -- the same sum, then one binary32
+  multiply by ``inv_w`` (the caller's inverse world size).
+* ``fold_into(dst, stage)``             -- ``dst + stage`` elementwise.
 
 Pins (tests/test_oracle_pins.py): exact-rational brute force with an explicit
 round-to-nearest-even, the binary64 double-path, hand-derived IEEE 754 cases in

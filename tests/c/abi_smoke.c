@@ -18,6 +18,10 @@ int main(void)
     printf("abi %d\n", detfold_abi_version());
     printf("w0 %d\n", fold_ranks(out, stacked, 0, 16, NULL));
     printf("overlap %d\n", fold_ranks((float *)stacked, stacked, 2, 16, NULL));
+    printf("timed_w0 %d\n", detfold_fold_ranks_timed(out, stacked, 0, 16, 0, 1.0f, NULL, NULL, NULL, NULL));
+    printf("timed_overlap %d\n",
+           detfold_fold_ranks_timed((float *)stacked, stacked, 2, 16, 1, 0.5f, NULL, NULL, NULL, NULL));
+    printf("timed_empty %d\n", detfold_fold_ranks_timed(out, stacked, 4, 0, 0, 1.0f, NULL, NULL, NULL, NULL));
     printf("empty %d\n", fold_into(NULL, NULL, 0, NULL));
     printf("strerror %s\n", detfold_strerror(DETFOLD_EOVERLAP));
     int rc = detfold_shard_plan(10, 3, start, length);

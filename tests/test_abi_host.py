@@ -47,7 +47,7 @@ def test_library_exports_nothing_but_the_c_abi(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 6
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 7
 
 
 def test_strerror_covers_every_code(detfold_lib):

@@ -25,6 +25,9 @@ def test_c99_caller(tmp_path, detfold_lib):
     assert lines["w0"] == str(detfold_lib.EINVAL)
     assert lines["overlap"] == str(detfold_lib.EOVERLAP)
     assert lines["empty"] == str(detfold_lib.OK)
+    assert lines["timed_w0"] == str(detfold_lib.EINVAL)
+    assert lines["timed_overlap"] == str(detfold_lib.EOVERLAP)
+    assert lines["timed_empty"] == str(detfold_lib.OK)
     assert "overlap" in lines["strerror"]
     assert lines["shards"] == "0 4 3 3"
     assert lines["plan"] == "0 %d 512 32768 128" % detfold_lib.PATH_ROWS

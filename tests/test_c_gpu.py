@@ -14,8 +14,7 @@ EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "fold_gpu")
 
 
 def test_c_caller_on_the_device(detfold_lib):
-    if not os.path.exists(EXE):
-        pytest.skip("tests/c/fold_gpu is not built; __graft_entry__.build() builds it")
+    assert os.path.exists(EXE), "tests/c/fold_gpu is not built; __graft_entry__.build() builds it"
     print("case: tests/c/fold_gpu", flush=True)
     res = subprocess.run([EXE], capture_output=True, text=True, timeout=100)
     print(res.stdout[-4000:], flush=True)

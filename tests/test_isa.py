@@ -15,7 +15,6 @@ gfx950 assembly it produced:
 import glob
 import os
 import re
-import subprocess
 
 import pytest
 
@@ -29,10 +28,7 @@ SCALAR_WRITE = re.compile(r"^\s*(s_store\w*|s_buffer_store\w*|s_atomic\w*|s_buff
 def isa(tmp_path_factory):
     from deterministic_fixed_order_amd import _build
     out = str(tmp_path_factory.mktemp("isa"))
-    try:
-        _build.save_temps(out)
-    except (OSError, subprocess.CalledProcessError) as e:  # pragma: no cover - no hipcc
-        pytest.skip("hipcc build failed: %s" % e)
+    _build.save_temps(out)  # a failed build fails every test here, never skips it
     files = sorted(glob.glob(os.path.join(out, "*gfx950*.s")))
     assert files, "no gfx950 assembly produced"
     return "\n".join(open(f).read() for f in files)

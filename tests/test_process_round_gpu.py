@@ -19,6 +19,11 @@ The one-shot test gives each of two processes its own rank's one-shot kernel
 (detfold_one_shot_rank); the staging buffers, barrier counters and refusal
 words are shared the same way, and the two kernels meet only through those
 counters.  Three rounds must double the sum twice, with both words zero.
+
+The shared tensors reach each child inside a one-element list that the child
+empties, so that its last reference to them is its own and it can drop them
+before it exits: the parent's record of what it shared is then released
+before the parent ends.
 """
 import os
 import socket
@@ -38,7 +43,16 @@ def _free_port():
         return s.getsockname()[1]
 
 
-def _rank_main(rank, arenas, n, port, world):
+def _release_shared():
+    """Free the mapped tensors a child dropped, while its device context lives."""
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.ipc_collect()
+
+
+def _rank_main(rank, box, n, port, world):
     import sys
     import torch
     import torch.distributed as dist
@@ -50,6 +64,7 @@ def _rank_main(rank, arenas, n, port, world):
     os.environ["MASTER_ADDR"] = "127.0.0.1"
     os.environ["MASTER_PORT"] = str(port)
     dist.init_process_group("gloo", rank=rank, world_size=world)
+    arenas = box.pop()
     try:
         torch.cuda.set_device(0)
         start, length = df.shard_plan(n, world)[rank]
@@ -67,6 +82,8 @@ def _rank_main(rank, arenas, n, port, world):
         torch.cuda.synchronize()
         dist.barrier()
     finally:
+        arenas = mine = a = None  # this child's last references to the shared arenas
+        _release_shared()
         dist.destroy_process_group()
 
 
@@ -81,14 +98,14 @@ def test_processes_fold_through_shared_arenas(detfold_lib, world, n):
     arenas = [torch.from_numpy(host[r]).to(dev) for r in range(world)]
     torch.cuda.synchronize()
     print("case: %d processes, n=%d" % (world, n), flush=True)
-    mp.spawn(_rank_main, args=(arenas, n, _free_port(), world), nprocs=world, join=True)
+    mp.spawn(_rank_main, args=([arenas], n, _free_port(), world), nprocs=world, join=True)
     torch.cuda.ipc_collect()  # release the handles the children held
     for r in range(world):
         got = arenas[r].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
 
 
-def _fused_rank_main(rank, arenas, n, port, world):
+def _fused_rank_main(rank, box, n, port, world):
     import sys
     import torch
     import torch.distributed as dist
@@ -100,6 +117,7 @@ def _fused_rank_main(rank, arenas, n, port, world):
     os.environ["MASTER_ADDR"] = "127.0.0.1"
     os.environ["MASTER_PORT"] = str(port)
     dist.init_process_group("gloo", rank=rank, world_size=world)
+    arenas = box.pop()
     try:
         torch.cuda.set_device(0)
         start, length = df.shard_plan(n, world)[rank]
@@ -110,6 +128,8 @@ def _fused_rank_main(rank, arenas, n, port, world):
         torch.cuda.synchronize()
         dist.barrier()
     finally:
+        arenas = None
+        _release_shared()
         dist.destroy_process_group()
 
 
@@ -129,14 +149,14 @@ def test_processes_fused_round_through_shared_arenas(detfold_lib, world, n):
     arenas = [torch.from_numpy(host[r]).to(dev) for r in range(world)]
     torch.cuda.synchronize()
     print("case: fused round in %d processes, n=%d" % (world, n), flush=True)
-    mp.spawn(_fused_rank_main, args=(arenas, n, _free_port(), world), nprocs=world, join=True)
+    mp.spawn(_fused_rank_main, args=([arenas], n, _free_port(), world), nprocs=world, join=True)
     torch.cuda.ipc_collect()
     for r in range(world):
         got = arenas[r].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "arena %d, n=%d" % (r, n)
 
 
-def _one_shot_rank_main(rank, xs, buffers, n, rounds, port, world):
+def _one_shot_rank_main(rank, box, n, rounds, port, world):
     import sys
     import torch
     import torch.distributed as dist
@@ -148,6 +168,8 @@ def _one_shot_rank_main(rank, xs, buffers, n, rounds, port, world):
     os.environ["MASTER_ADDR"] = "127.0.0.1"
     os.environ["MASTER_PORT"] = str(port)
     dist.init_process_group("gloo", rank=rank, world_size=world)
+    xs, buffers = box.pop()
+    link = None
     try:
         torch.cuda.set_device(0)
         link = df.OneShotLink(n, device="cuda:0", buffers=buffers, init=False)
@@ -162,6 +184,8 @@ def _one_shot_rank_main(rank, xs, buffers, n, rounds, port, world):
             torch.cuda.synchronize()
         dist.barrier()
     finally:
+        xs = buffers = link = None
+        _release_shared()
         dist.destroy_process_group()
 
 
@@ -184,7 +208,7 @@ def test_one_shot_ranks_as_processes(detfold_lib, n):
     xs = [torch.from_numpy(ha).to(dev), torch.from_numpy(hb).to(dev)]
     torch.cuda.synchronize()
     print("case: one-shot ranks as 2 processes, n=%d, %d rounds" % (n, rounds), flush=True)
-    mp.spawn(_one_shot_rank_main, args=(xs, (link.stage, link.flags, link.words), n, rounds,
+    mp.spawn(_one_shot_rank_main, args=([(xs, (link.stage, link.flags, link.words))], n, rounds,
                                         _free_port(), 2), nprocs=2, join=True)
     torch.cuda.ipc_collect()
     assert link.barrier_words() == [0, 0]
