@@ -30,10 +30,11 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdetfold.so")
 
-OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE = 0, 1, 2, 3, 4
+OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE, ESIZE = 0, 1, 2, 3, 4, 5
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 7
+ABI_VERSION = 8
+STATIC_STAGE_FLOATS = 1 << 22
 ONE_SHOT_BLOCKS = 64
 ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
 BARRIER_ENTRY_EXPIRED, BARRIER_EXIT_EXPIRED = 40043, 40044
@@ -45,7 +46,7 @@ EXPORTS = (
     "detfold_fold_ranks_ex", "fold_slots", "fold_slots_scaled", "detfold_loopback_round",
     "detfold_pair_link_init", "detfold_pair_all_reduce", "detfold_pair_broadcast",
     "detfold_pair_all_gather", "detfold_one_shot_init", "detfold_one_shot_all_reduce",
-    "detfold_one_shot_rank", "detfold_fold_ranks_timed",
+    "detfold_one_shot_rank", "detfold_fold_ranks_timed", "detfold_loopback_round_static",
 )
 
 
@@ -115,6 +116,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fold_slots.argtypes = [f32p, pp, i32, i64, vp]
     lib.fold_slots_scaled.argtypes = [f32p, pp, i32, i64, ctypes.c_float, vp]
     lib.detfold_loopback_round.argtypes = [pp, i32, i64, f32p, i64, i32, vp]
+    lib.detfold_loopback_round_static.argtypes = [pp, i32, i64, i32, vp]
     lib.detfold_pair_link_init.argtypes = [ctypes.POINTER(PairLinkC)]
     lib.detfold_pair_all_reduce.argtypes = [ctypes.POINTER(PairLinkC), f32p, f32p, i64]
     lib.detfold_pair_broadcast.argtypes = [ctypes.POINTER(PairLinkC), i32, f32p, f32p, i64]
@@ -305,6 +307,24 @@ def loopback_round(arenas, stage=None, *, reverse_delivery: bool = False, direct
     _check(load().detfold_loopback_round(_ptr_array(arenas), len(arenas), n, stage_ptr, stage_elems,
                                          flags, _stream_handle(arenas[0], stream)),
            "loopback_round")
+
+
+def loopback_round_static(arenas, *, reverse_delivery: bool = False, stream=None) -> None:
+    """The staged ``loopback_round`` with the library's own static stage
+    (``STATIC_STAGE_FLOATS`` floats per device): nothing is allocated.  W *
+    ceil(n / W) must fit the stage (else ``ESIZE``); calls that overlap in time
+    on one device race on the stage."""
+    if not arenas:
+        raise ValueError("need at least one arena")
+    n = arenas[0].numel()
+    for i, a in enumerate(arenas):
+        _f32_device(a, "arenas[%d]" % i)
+        if a.numel() != n:
+            raise ValueError("arena %d has %d elements, arena 0 has %d" % (i, a.numel(), n))
+    _check(load().detfold_loopback_round_static(_ptr_array(arenas), len(arenas), n,
+                                                ROUND_REVERSE_DELIVERY if reverse_delivery else 0,
+                                                _stream_handle(arenas[0], stream)),
+           "loopback_round_static")
 
 
 class PairLink:

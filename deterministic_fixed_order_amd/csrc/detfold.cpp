@@ -311,6 +311,8 @@ const char *detfold_strerror(int rc)
     case DETFOLD_EOVERLAP: return "output overlaps an input range";
     case DETFOLD_ELAUNCH: return "HIP kernel launch failed";
     case DETFOLD_EDEVICE: return "no usable current HIP device";
+    case DETFOLD_ESIZE: return "request exceeds the library's static stage "
+                               "(DETFOLD_STATIC_STAGE_FLOATS floats)";
     default: return "unknown detfold return code";
     }
 }
@@ -363,6 +365,26 @@ int detfold_loopback_round(float *const *arenas, int32_t W, int64_t n, float *st
 {
     int rc = check_round_args(arenas, W, n, stage, stage_elems, flags);
     if (rc != DETFOLD_OK || W == 1 || n == 0)
+        return rc;
+    return run_round(arenas, W, n, stage, flags, static_cast<hipStream_t>(stream));
+}
+
+int detfold_loopback_round_static(float *const *arenas, int32_t W, int64_t n, int32_t flags,
+                                  void *stream)
+{
+    if (flags & ~DETFOLD_ROUND_REVERSE_DELIVERY)
+        return DETFOLD_EINVAL;  // the staged round only
+    // the arenas alone first (no stage yet: DIRECT skips the stage checks)
+    int rc = check_round_args(arenas, W, n, nullptr, 0, flags | DETFOLD_ROUND_DIRECT);
+    if (rc != DETFOLD_OK || W == 1 || n == 0)
+        return rc;
+    const int64_t need = (int64_t)W * ((n + W - 1) / W);
+    if (need > DETFOLD_STATIC_STAGE_FLOATS)
+        return DETFOLD_ESIZE;
+    float *stage = nullptr;
+    if ((rc = static_stage(&stage)) != DETFOLD_OK)
+        return rc;
+    if ((rc = check_round_args(arenas, W, n, stage, DETFOLD_STATIC_STAGE_FLOATS, flags)) != DETFOLD_OK)
         return rc;
     return run_round(arenas, W, n, stage, flags, static_cast<hipStream_t>(stream));
 }

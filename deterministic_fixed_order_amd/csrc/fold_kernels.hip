@@ -37,9 +37,16 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "internal.h"
+
+// The stage of detfold_loopback_round_static: device memory the library owns,
+// one copy per device, held until the process ends.  Host code never uses
+// this name as an address (on the host it is only a stand-in); it takes each
+// device's address from hipGetSymbolAddress (static_stage below).
+static __device__ __align__(256) float scratch[DETFOLD_STATIC_STAGE_FLOATS];
 
 namespace detfold_impl {
 namespace {
@@ -843,6 +850,31 @@ int launch_copy(float *const *dsts, int ndst, const float *src, int64_t len, int
                   static_cast<hipEvent_t>(done)) == hipSuccess
                ? DETFOLD_OK
                : DETFOLD_ELAUNCH;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int static_stage(float **stage)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<float *> cached[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return DETFOLD_EDEVICE;
+    if (dev < kMaxDevices) {
+        float *p = cached[dev].load(std::memory_order_acquire);
+        if (p) {
+            *stage = p;
+            return DETFOLD_OK;
+        }
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return DETFOLD_EDEVICE;
+    if (dev < kMaxDevices)
+        cached[dev].store(static_cast<float *>(p), std::memory_order_release);
+    *stage = static_cast<float *>(p);
+    return DETFOLD_OK;
 }
 
 int launch_one_shot(const OneShotArgs &a, int nranks, void *stream)

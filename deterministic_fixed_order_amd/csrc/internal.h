@@ -175,6 +175,9 @@ int launch_copy(float *const *dsts, int ndst, const float *src, int64_t len, int
 // `p` is the plan make_plan gives that geometry.
 int launch_rows_all(const Geometry &g, const detfold_plan &p, void *stream);
 int launch_one_shot(const OneShotArgs &a, int nranks, void *stream);
+// The current device's address of the library's static stage
+// (DETFOLD_STATIC_STAGE_FLOATS floats), or DETFOLD_EDEVICE.
+int static_stage(float **stage);
 int launch_zero_words(uint32_t *p, int64_t n, void *stream);
 
 }  // namespace detfold_impl

@@ -52,6 +52,7 @@ extern "C" {
 #define DETFOLD_EOVERLAP 2 /* output range overlaps an input range it must not alias     */
 #define DETFOLD_ELAUNCH 3  /* the HIP launch was refused                                 */
 #define DETFOLD_EDEVICE 4  /* no current HIP device, or its properties could not be read */
+#define DETFOLD_ESIZE 5    /* the request needs more than the library's static stage     */
 
 /*
  * fold_ranks -- out[i] = ((s_0[i] + s_1[i]) + ...) + s_{W-1}[i]
@@ -164,6 +165,31 @@ int fold_slots_scaled(float *out, const float *const *slots, int32_t W, int64_t 
 #define DETFOLD_ROUND_FUSED 4
 int detfold_loopback_round(float *const *arenas, int32_t W, int64_t n, float *stage,
                            int64_t stage_elems, int32_t flags, void *stream);
+
+/*
+ * detfold_loopback_round_static -- the staged detfold_loopback_round with its
+ * stage in device memory the library owns, for callers that cannot allocate
+ * device memory (code under stream or graph capture, tight serving loops,
+ * harnesses that forbid allocation): the call allocates nothing and frees
+ * nothing.  The stage is a file-scope device array of
+ * DETFOLD_STATIC_STAGE_FLOATS floats (16 MiB), one per device the library
+ * runs on, held until the process ends.
+ *   arenas, W, n  as detfold_loopback_round; W * ceil(n / W) must not exceed
+ *                 DETFOLD_STATIC_STAGE_FLOATS, else DETFOLD_ESIZE before any
+ *                 device work
+ *   flags         0 or DETFOLD_ROUND_REVERSE_DELIVERY (the staged round;
+ *                 anything else is DETFOLD_EINVAL)
+ * The bits equal detfold_loopback_round's with a caller stage.  The stage is
+ * shared by every call on a device and keeps the last call's contents; every
+ * call overwrites the part it reads before reading it, so nothing needs
+ * clearing.  Calls that overlap in time on one device (other streams, other
+ * threads, other processes do not share it) race on the stage: order them.
+ * Errors: as detfold_loopback_round, plus DETFOLD_ESIZE, and DETFOLD_EDEVICE
+ * when the stage's device address cannot be obtained.
+ */
+#define DETFOLD_STATIC_STAGE_FLOATS (1 << 22)
+int detfold_loopback_round_static(float *const *arenas, int32_t W, int64_t n, int32_t flags,
+                                  void *stream);
 
 /*
  * A two-rank all-reduce on one device: the pipeline arm of memra-engine
@@ -298,7 +324,7 @@ int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 7
+#define DETFOLD_ABI_VERSION 8
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------

@@ -47,12 +47,12 @@ def test_library_exports_nothing_but_the_c_abi(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 7
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 8
 
 
 def test_strerror_covers_every_code(detfold_lib):
     seen = set()
-    for rc in range(0, 5):
+    for rc in range(0, 6):
         s = detfold_lib.strerror(rc)
         assert s and s not in seen
         seen.add(s)
@@ -483,3 +483,24 @@ def test_plan_sixteen_slot_shape_follows_alignment(detfold_lib, n):
     for plan in (p, q):
         assert plan["path"] == detfold_lib.PATH_ROWS
         assert plan["grid"] == -(-plan["body"] // plan["tile"])
+
+
+def test_static_round_rejects_before_any_device_work(detfold_lib):
+    # every rejection here happens before the library looks up its stage
+    lib = detfold_lib.load()
+    EINVAL, EOVERLAP, ESIZE, OK = detfold_lib.EINVAL, detfold_lib.EOVERLAP, detfold_lib.ESIZE, detfold_lib.OK
+    cap = detfold_lib.STATIC_STAGE_FLOATS
+    ar = [BASE + i * (1 << 26) for i in range(4)]
+    for flags in (detfold_lib.ROUND_DIRECT, detfold_lib.ROUND_FUSED, 8,
+                  detfold_lib.ROUND_DIRECT | detfold_lib.ROUND_REVERSE_DELIVERY):
+        assert lib.detfold_loopback_round_static(_ptrs(*ar), 4, 1000, flags, None) == EINVAL
+    assert lib.detfold_loopback_round_static(_ptrs(*ar), 0, 1000, 0, None) == EINVAL
+    assert lib.detfold_loopback_round_static(_ptrs(*ar), 4, -1, 0, None) == EINVAL
+    assert lib.detfold_loopback_round_static(_ptrs(ar[0], ar[1] + 2, ar[2], ar[3]), 4, 1000, 0, None) == EINVAL
+    assert lib.detfold_loopback_round_static(_ptrs(ar[0], ar[0] + 8, ar[2], ar[3]), 4, 1000, 0,
+                                             None) == EOVERLAP
+    assert lib.detfold_loopback_round_static(_ptrs(*ar), 4, cap + 1, 0, None) == ESIZE
+    assert lib.detfold_loopback_round_static(_ptrs(*ar[:3]), 3, cap, 1, None) == ESIZE  # 3*ceil(n/3) > cap
+    assert lib.detfold_loopback_round_static(_ptrs(*ar[:1]), 1, 10 ** 9, 0, None) == OK  # one rank
+    assert lib.detfold_loopback_round_static(_ptrs(*ar), 4, 0, 0, None) == OK            # empty
+    assert "static stage" in detfold_lib.strerror(ESIZE)
