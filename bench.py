@@ -300,7 +300,7 @@ def bench_fold(args, torch, df, dev):
     else:
         result["bit_exact_vs_oracle"] = oracle_check(host, inv_w, out)
     if args.workload == "w8" and args.secondary:
-        del host, stacked, out
+        del host, stacked, out, step
         torch.cuda.empty_cache()
         result["secondary"] = {w: bench_secondary(args, torch, df, dev, w) for w in ("w4", "w16")}
     return result
@@ -316,6 +316,7 @@ def bench_secondary(args, torch, df, dev, name):
     stream = torch.cuda.current_stream(dev)
     timer = Timer(torch, stream)
     step = fold_step(df, out, stacked, inv_w)
+    settle(timer, step)
     for _ in range(args.warmup):
         step()
     ms = timer.region(step, args.steps) / args.steps
@@ -341,41 +342,57 @@ def bench_secondary(args, torch, df, dev, name):
 
 
 def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step):
-    """Single launches, each after writing a 1 GiB scrub buffer (more than
-    four times the 256 MB memory-side cache, so it holds none of the fold's
-    operands when the call starts).  Every call is timed twice at once: by an
-    event pair recorded around it on the stream (launch and event latency
-    included), and by the start/stop events its own dispatch records (the
-    kernel alone)."""
+    """Single launches, each after a 1 GiB scrub (more than four times the
+    256 MB memory-side cache, so it holds none of the fold's operands when the
+    call starts).  Two scrubs: writing the buffer and then reading it back
+    (the cache is left holding clean lines), and writing it only (the cache
+    is left holding dirty lines, whose write-back then competes with the
+    fold).  Every call is timed twice at once: by an event pair recorded
+    around it on the stream (launch and event latency included), and by the
+    start/stop events its own dispatch records (the kernel alone)."""
     stream = timer.stream
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    pairs = timing_events(torch, stream, args.singles)
-    outer, inner = [], []
-    for i, (a, b) in enumerate(pairs):
-        scrub.fill_(float(i))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        df.fold_ranks_timed(out, stacked, a, b, scaled=inv_w is not None,
-                            inv_w=inv_w if inv_w is not None else 1.0)
-        e1.record(stream)
-        e1.synchronize()
-        outer.append(e0.elapsed_time(e1))
-        inner.append(a.elapsed_time(b))
+    gb = lambda ms: round(bytes_per_step / (ms * 1e-3) / 1e9, 2)
+    res = {"calls": args.singles}
+    for key, read_back in (("write_then_read_scrub", True), ("write_scrub", False)):
+        pairs = timing_events(torch, stream, args.singles)
+        outer, inner = [], []
+        for i, (a, b) in enumerate(pairs):
+            scrub.fill_(float(i))
+            if read_back:
+                scrub.amax()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            df.fold_ranks_timed(out, stacked, a, b, scaled=inv_w is not None,
+                                inv_w=inv_w if inv_w is not None else 1.0)
+            e1.record(stream)
+            e1.synchronize()
+            outer.append(e0.elapsed_time(e1))
+            inner.append(a.elapsed_time(b))
+        med_o, med_i = statistics.median(outer), statistics.median(inner)
+        log("single launches after a 1 GiB %s: event pair around the call median %.4f ms (%.1f GB/s), "
+            "kernel alone median %.4f ms (%.1f GB/s)" % (key.replace("_", " "), med_o, gb(med_o), med_i,
+                                                           gb(med_i)))
+        res[key] = {"kernel_only_median_ms": round(med_i, 6), "kernel_only_best_ms": round(min(inner), 6),
+                    "kernel_only_median_GBps": gb(med_i), "kernel_only_frac": round(gb(med_i) / HBM_PEAK_GBS, 4),
+                    "event_pair_median_ms": round(med_o, 6), "event_pair_best_ms": round(min(outer), 6),
+                    "event_pair_median_GBps": gb(med_o)}
     del scrub
     torch.cuda.synchronize()
-    med_o, med_i = statistics.median(outer), statistics.median(inner)
-    gb = lambda ms: round(bytes_per_step / (ms * 1e-3) / 1e9, 2)
-    log("single launches after a 1 GiB scrub write: event pair around the call median %.4f ms "
-        "(%.1f GB/s), kernel alone median %.4f ms (%.1f GB/s)" % (med_o, gb(med_o), med_i, gb(med_i)))
-    return {"calls": len(outer), "scrub": "1 GiB written (fill) before each call",
-            "kernel_only_median_ms": round(med_i, 6), "kernel_only_best_ms": round(min(inner), 6),
-            "kernel_only_median_GBps": gb(med_i),
-            "kernel_only_frac": round(gb(med_i) / HBM_PEAK_GBS, 4),
-            "event_pair_median_ms": round(med_o, 6), "event_pair_best_ms": round(min(outer), 6),
-            "event_pair_median_GBps": gb(med_o),
-            "note": "kernel_only: start/stop events recorded by the fold's own dispatch; event_pair: "
-                    "events recorded on the stream before and after the call"}
+    res["note"] = ("kernel_only: start/stop events recorded by the fold's own dispatch; event_pair: events "
+                   "recorded on the stream before and after the call; scrub: 1 GiB filled (and, in the "
+                   "first set, then read back with amax) before each call")
+    return res
+
+
+def settle(timer, step, target_ms=100.0):
+    """Untimed calls for about target_ms, so that clocks that dropped while
+    the device idled (host-side setup, the CPU oracle) are back up before a
+    timed region starts."""
+    ms = timer.region(step, 3) / 3
+    for _ in range(min(2000, int(target_ms / max(ms, 1e-3)))):
+        step()
 
 
 def bench_ceiling(args, torch, dev, timer, stacked, out):
@@ -438,32 +455,48 @@ def device_info(torch, dev):
 def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     """The owner-shard form of the offset arena: each of the W owners' shards
     is gathered once (untimed, device copies of the W slices) into a [W][l_p]
-    scratch, then the W shard folds run back to back per step into one output
-    at the owners' offsets, which must equal the whole-arena fold bit for bit.
-    Same algorithmic bytes as the whole fold, in W launches."""
+    scratch; then per step all W shard folds run into one output at the
+    owners' offsets, once as W separate fold_ranks launches and once as one
+    fold_ranks_batch launch.  Both must equal the whole-arena fold bit for
+    bit.  Same algorithmic bytes as the whole fold."""
     import torch as _torch
     shards = df.shard_plan(n, W)
     scratch = [_torch.empty((W, l), dtype=_torch.float32, device=out.device) for _, l in shards]
     for (s, l), sc in zip(shards, scratch):
         sc.copy_(stacked[:, s:s + l])
-    out_sh = _torch.empty_like(out)
+    out_sep, out_one = _torch.empty_like(out), _torch.empty_like(out)
+    views_sep = [out_sep[s:s + l] for s, l in shards]
+    views_one = [out_one[s:s + l] for s, l in shards]
 
-    def step():
-        for (s, l), sc in zip(shards, scratch):
-            df.fold_ranks(out_sh[s:s + l], sc)
-    for _ in range(args.warmup):
-        step()
-    ms = timer.region(step, args.steps) / args.steps
+    def separate():
+        for o, sc in zip(views_sep, scratch):
+            df.fold_ranks(o, sc)
+
+    def one_launch():
+        df.fold_ranks_batch(views_one, scratch)
+    moved = (W + 1) * n * 4
+    res = {"shards": W, "shard_len_max": max(l for _, l in shards),
+           "note": "shards gathered once by device copies (untimed); per step every shard fold, "
+                   "as separate launches and as one batched launch"}
+    for key, fn in (("separate_launches", separate), ("one_launch", one_launch)):
+        settle(timer, fn)
+        for _ in range(args.warmup):
+            fn()
+        ms = timer.region(fn, args.steps) / args.steps
+        gbs = moved / (ms * 1e-3) / 1e9
+        res[key] = {"ms_per_set": round(ms, 5), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     _torch.cuda.synchronize()
-    same = bool(_torch.equal(out_sh.view(_torch.int32), out.view(_torch.int32)))
-    gbs = (W + 1) * n * 4 / (ms * 1e-3) / 1e9
-    log("owner shards: %d shard folds of about %d elements, %.4f ms per set (%.1f GB/s), bits equal "
-        "to the whole fold: %s" % (W, shards[0][1], ms, gbs, same))
-    if not same:
+    same_sep = bool(_torch.equal(out_sep.view(_torch.int32), out.view(_torch.int32)))
+    same_one = bool(_torch.equal(out_one.view(_torch.int32), out.view(_torch.int32)))
+    res["separate_launches"]["bits_equal_whole_fold"] = same_sep
+    res["one_launch"]["bits_equal_whole_fold"] = same_one
+    log("owner shards: %d shard folds of about %d elements: %d launches %.4f ms per set (%.1f GB/s), one "
+        "batched launch %.4f ms (%.1f GB/s); bits equal to the whole fold: %s / %s"
+        % (W, shards[0][1], W, res["separate_launches"]["ms_per_set"], res["separate_launches"]["GBps"],
+           res["one_launch"]["ms_per_set"], res["one_launch"]["GBps"], same_sep, same_one))
+    if not (same_sep and same_one):
         raise RuntimeError("the owner-shard folds differ from the whole-arena fold")
-    return {"shards": W, "shard_len_max": max(l for _, l in shards), "ms_per_set": round(ms, 5),
-            "GBps": round(gbs, 1), "bits_equal_whole_fold": same,
-            "note": "shards gathered once by device copies (untimed); the W shard folds timed back to back"}
+    return res
 
 
 def bench_alternating(args, torch, df, dev, timer, stacked, out, bytes_per_step):

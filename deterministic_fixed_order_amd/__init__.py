@@ -13,6 +13,7 @@ PyTorch is used for device memory and streams only.
     fold_ranks_scaled(out, stacked, inv_w)   the same, then * inv_w
     fold_into(dst, stage)                    dst = dst + stage (in place)
     fold_slots(out, [s_0, ..., s_{W-1}])     the fold over separate buffers (W <= 16)
+    fold_ranks_batch(outs, stackeds)         many stacked folds of one width in one launch
     loopback_round(arenas, stage=None, ...)  one reduction round over W arenas (staged, direct, fused)
     PairLink(...).all_reduce(x0, x1)         two-stream (two-rank) all-reduce on one device
     PairLink(...).broadcast / all_gather     pure movement between the two ranks
@@ -33,7 +34,7 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE, ESIZE = 0, 1, 2, 3, 4, 5
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 8
+ABI_VERSION = 9
 STATIC_STAGE_FLOATS = 1 << 22
 ONE_SHOT_BLOCKS = 64
 ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
@@ -47,7 +48,9 @@ EXPORTS = (
     "detfold_pair_link_init", "detfold_pair_all_reduce", "detfold_pair_broadcast",
     "detfold_pair_all_gather", "detfold_one_shot_init", "detfold_one_shot_all_reduce",
     "detfold_one_shot_rank", "detfold_fold_ranks_timed", "detfold_loopback_round_static",
+    "fold_ranks_batch", "fold_ranks_batch_scaled", "detfold_plan_fold_ranks_batch",
 )
+MAX_JOBS = 32
 
 
 class DetfoldError(RuntimeError):
@@ -59,6 +62,10 @@ class DetfoldError(RuntimeError):
 class Launch(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32), ("policy", ctypes.c_int32)]
+
+
+class FoldJob(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("stacked", ctypes.c_void_p), ("len", ctypes.c_int64)]
 
 
 class PairLinkC(ctypes.Structure):
@@ -117,6 +124,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fold_slots_scaled.argtypes = [f32p, pp, i32, i64, ctypes.c_float, vp]
     lib.detfold_loopback_round.argtypes = [pp, i32, i64, f32p, i64, i32, vp]
     lib.detfold_loopback_round_static.argtypes = [pp, i32, i64, i32, vp]
+    jp = ctypes.POINTER(FoldJob)
+    lib.fold_ranks_batch.argtypes = [jp, i32, i32, vp]
+    lib.fold_ranks_batch_scaled.argtypes = [jp, i32, i32, ctypes.c_float, vp]
+    lib.detfold_plan_fold_ranks_batch.argtypes = [jp, i32, i32, i32, ctypes.POINTER(Plan)]
     lib.detfold_pair_link_init.argtypes = [ctypes.POINTER(PairLinkC)]
     lib.detfold_pair_all_reduce.argtypes = [ctypes.POINTER(PairLinkC), f32p, f32p, i64]
     lib.detfold_pair_broadcast.argtypes = [ctypes.POINTER(PairLinkC), i32, f32p, f32p, i64]
@@ -211,6 +222,35 @@ def fold_into(dst, stage, stream=None) -> None:
         raise ValueError("dst and stage are on different devices")
     _check(load().fold_into(dst.data_ptr(), stage.data_ptr(), dst.numel(),
                             _stream_handle(dst, stream)), "fold_into")
+
+
+def _jobs(outs, stackeds):
+    if len(outs) != len(stackeds):
+        raise ValueError("%d outputs for %d arenas" % (len(outs), len(stackeds)))
+    if len(outs) > MAX_JOBS:
+        raise ValueError("at most %d jobs per call, got %d" % (MAX_JOBS, len(outs)))
+    W = None
+    jobs = (FoldJob * max(len(outs), 1))()
+    for j, (out, stacked) in enumerate(zip(outs, stackeds)):
+        w, n = _stacked_shape(out, stacked)
+        if W is not None and w != W:
+            raise ValueError("job %d has W=%d, job 0 has W=%d" % (j, w, W))
+        W = w
+        jobs[j].out, jobs[j].stacked, jobs[j].len = out.data_ptr(), stacked.data_ptr(), n
+    return jobs, len(outs), (W or 1)
+
+
+def fold_ranks_batch(outs, stackeds, inv_w: Optional[float] = None, stream=None) -> None:
+    """``fold_ranks(outs[j], stackeds[j])`` for every j (same W), in one launch
+    where 2 <= W <= 16; with ``inv_w``, ``fold_ranks_scaled`` instead."""
+    jobs, count, W = _jobs(outs, stackeds)
+    if count == 0:
+        return
+    h = _stream_handle(outs[0], stream)
+    if inv_w is None:
+        _check(load().fold_ranks_batch(jobs, count, W, h), "fold_ranks_batch")
+    else:
+        _check(load().fold_ranks_batch_scaled(jobs, count, W, float(inv_w), h), "fold_ranks_batch_scaled")
 
 
 def fold_ranks_ex(out, stacked, *, scaled: bool = False, inv_w: float = 1.0, path: int = 0,
@@ -467,6 +507,18 @@ def plan_fold_ranks(out_addr: int, stacked_addr: int, W: int, n: int, cu_count: 
     cfg = ctypes.byref(Launch(**launch)) if launch else None
     _check(load().detfold_plan_fold_ranks(out_addr, stacked_addr, W, n, cu_count, cfg,
                                           ctypes.byref(p)), "plan_fold_ranks")
+    return p.as_dict()
+
+
+def plan_fold_ranks_batch(jobs: list, W: int, cu_count: int) -> dict:
+    """The plan of ``fold_ranks_batch``'s one launch (host only): ``jobs`` is a
+    list of ``(out_addr, stacked_addr, len)``."""
+    arr = (FoldJob * max(len(jobs), 1))()
+    for j, (o, st, n) in enumerate(jobs):
+        arr[j].out, arr[j].stacked, arr[j].len = o, st, n
+    p = Plan()
+    _check(load().detfold_plan_fold_ranks_batch(arr, len(jobs), W, cu_count, ctypes.byref(p)),
+           "plan_fold_ranks_batch")
     return p.as_dict()
 
 

@@ -252,6 +252,35 @@ int run_one_shot(const detfold_one_shot_link *k, int32_t rank0, int nranks, floa
     return launch_one_shot(one_shot_args(k, rank0, nranks, xa, xb, n), nranks, stream);
 }
 
+// Many stacked folds of one width: one launch of the batched row body for
+// 2 <= W <= 16, else one launch per job.
+int run_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, bool scaled, float inv_w,
+              void *stream)
+{
+    int rc = check_batch_args(jobs, count, W);
+    if (rc != DETFOLD_OK)
+        return rc;
+    bool any = false;
+    for (int32_t j = 0; j < count; ++j)
+        any = any || jobs[j].len > 0;
+    if (!any)
+        return DETFOLD_OK;
+    if (W == 1 || W > kMaxRowsW) {  // no batched body: one launch per job
+        for (int32_t j = 0; j < count && rc == DETFOLD_OK; ++j)
+            rc = run_ranks(jobs[j].out, jobs[j].stacked, W, jobs[j].len, scaled, inv_w, nullptr, stream);
+        return rc;
+    }
+    int32_t cu = 0;
+    if ((rc = current_cu_count(&cu)) != DETFOLD_OK)
+        return rc;
+    BatchArgs a;
+    detfold_plan p;
+    if ((rc = plan_batch(jobs, count, W, cu, &a, &p)) != DETFOLD_OK)
+        return rc;
+    a.inv_w = inv_w;
+    return launch_batch(a, W, p, scaled, stream);
+}
+
 }  // namespace
 }  // namespace detfold_impl
 
@@ -285,6 +314,29 @@ int detfold_fold_ranks_timed(float *out, const float *stacked, int32_t W, int64_
                              void *stop)
 {
     return run_ranks(out, stacked, W, len, scaled != 0, inv_w, launch, stream, start, stop);
+}
+
+int fold_ranks_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, void *stream)
+{
+    return run_batch(jobs, count, W, false, 1.0f, stream);
+}
+
+int fold_ranks_batch_scaled(const detfold_fold_job *jobs, int32_t count, int32_t W, float inv_w,
+                            void *stream)
+{
+    return run_batch(jobs, count, W, true, inv_w, stream);
+}
+
+int detfold_plan_fold_ranks_batch(const detfold_fold_job *jobs, int32_t count, int32_t W,
+                                  int32_t cu_count, detfold_plan *plan)
+{
+    if (!plan || W < 2 || W > kMaxRowsW)
+        return DETFOLD_EINVAL;
+    int rc = check_batch_args(jobs, count, W);
+    if (rc != DETFOLD_OK)
+        return rc;
+    BatchArgs a;
+    return plan_batch(jobs, count, W, cu_count, &a, plan);
 }
 
 int fold_into(float *dst, const float *stage, int64_t n, void *stream)

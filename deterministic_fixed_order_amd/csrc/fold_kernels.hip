@@ -265,14 +265,26 @@ template <int W, int SPW> struct RowsShape {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int W, bool SCALED>
-__device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slots, int64_t i,
-                                               float inv_w)
+// Where slot r starts: a table of base pointers passed in the kernel
+// arguments, or, for the batched fold, base + r*len computed in scalar
+// registers (a table built in the kernel would live in private memory).
+struct TableSlots {
+    const SlotTable &t;
+    __device__ const float *operator()(int r) const { return t.p[r]; }
+};
+struct StrideSlots {
+    const float *s0;
+    int64_t len;
+    __device__ const float *operator()(int r) const { return s0 + (int64_t)r * len; }
+};
+
+template <int W, bool SCALED, typename Slots>
+__device__ __forceinline__ void fold_one_table(float *out, const Slots &slot, int64_t i, float inv_w)
 {
-    float acc = slots.p[0][i];
+    float acc = slot(0)[i];
 #pragma unroll
     for (int r = 1; r < W; ++r)
-        acc = acc + slots.p[r][i];
+        acc = acc + slot(r)[i];
     if constexpr (SCALED)
         acc = acc * inv_w;
     out[i] = acc;
@@ -281,8 +293,8 @@ __device__ __forceinline__ void fold_one_table(float *out, const SlotTable &slot
 // Wave `wave` streams the tile's bytes of its slots (wave*SPW .. wave*SPW+SPW-1
 // that exist) into their LDS rows: LPW KiB of each, through a descriptor based
 // at the slot's element e0 and limited to the tile's cnt groups.
-template <int W, int SPW, int LPW, int T>
-__device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const SlotTable &slots, int64_t e0,
+template <int W, int SPW, int LPW, int T, typename Slots>
+__device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const Slots &slot, int64_t e0,
                                             int64_t cnt, uint32_t wave, uint32_t lane)
 {
 #pragma unroll
@@ -290,7 +302,7 @@ __device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const SlotTable &s
         const uint32_t r = wave * SPW + j;
         if (r >= (uint32_t)W)
             break;  // an odd width's last wave streams one slot
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot(r) + e0, (uint32_t)(cnt * 16));
 #pragma unroll
         for (int u = 0; u < LPW; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&rows[r][u * 64], 16,
@@ -299,41 +311,88 @@ __device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const SlotTable &s
     }
 }
 
+// One tile of the row body: the W slots' bytes for groups [tile*T, tile*T+cnt)
+// of `out` streamed into the rows, then every thread folds whole groups in
+// ascending row order and stores them.  Every thread of the workgroup calls
+// it (it holds two barriers); a tile at or past `groups` does nothing.
+template <int W, int SPW, bool SCALED, int T, typename Slots>
+__device__ __forceinline__ void rows_tile(f4 (&rows)[W][T], float *out, const Slots &slots,
+                                          int64_t groups, int64_t head, int64_t tile, float inv_w,
+                                          uint32_t wave, uint32_t lane)
+{
+    constexpr int LPW = RowsShape<W, SPW>::LPW;
+    static_assert(T == RowsShape<W, SPW>::T, "the rows hold one tile");
+    constexpr int NT = RowsShape<W, SPW>::WAVES * 64;  // threads per workgroup
+    const int64_t g0 = tile * T;
+    if (g0 >= groups)
+        return;
+    const int64_t cnt = groups - g0 < T ? groups - g0 : T;
+    const int64_t e0 = head + 4 * g0;  // first element of the tile; out + e0 is 16-byte aligned
+    stream_rows<W, SPW, LPW, T>(rows, slots, e0, cnt, wave, lane);
+    __syncthreads();  // every row has landed
+
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + e0, (uint32_t)(cnt * 16));
+    for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += NT) {
+        f4 acc = rows[0][t];
+#pragma unroll
+        for (int q = 1; q < W; ++q)
+            acc = acc + rows[q][t];  // ascending slot order, one rounding per add
+        if constexpr (SCALED)
+            acc = acc * inv_w;  // one rounding of the finished sum
+        bstore<Aux<kStream>::store>(acc, ro, t * 16u);
+    }
+    __syncthreads();  // the rows are refilled only after every thread has read them
+}
+
+// The up to 3 elements before out's first 16-byte boundary (head) and after
+// its last (tail), one per thread: thread `k` < head + tail folds one.
+template <int W, bool SCALED, typename Slots>
+__device__ __forceinline__ void rows_edges(float *out, const Slots &slots, int64_t len, int64_t head,
+                                           int64_t k, float inv_w)
+{
+    const int64_t groups = (len - head) >> 2;
+    const int64_t tail0 = head + (groups << 2);
+    if (k < head + (len - tail0))
+        fold_one_table<W, SCALED>(out, slots, k < head ? k : tail0 + (k - head), inv_w);
+}
+
 template <int W, int SPW, bool SCALED>
 __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
                                                             int64_t head, float inv_w)
 {
-    constexpr int LPW = RowsShape<W, SPW>::LPW, T = RowsShape<W, SPW>::T;
-    constexpr int NT = RowsShape<W, SPW>::WAVES * 64;  // threads per workgroup
+    constexpr int T = RowsShape<W, SPW>::T;
     __shared__ f4 rows[W][T];
-
+    const TableSlots slot{slots};
+    rows_edges<W, SCALED>(out, slot, len, head, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, inv_w);
     const int64_t groups = (len - head) >> 2;
-    const int64_t tail0 = head + (groups << 2);
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid < head + (len - tail0))
-        fold_one_table<W, SCALED>(out, slots, gid < head ? gid : tail0 + (gid - head), inv_w);
-
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
-        const int64_t g0 = tile * T;
-        const int64_t cnt = groups - g0 < T ? groups - g0 : T;
-        const int64_t e0 = head + 4 * g0;  // first element of the tile; out + e0 is 16-byte aligned
-        stream_rows<W, SPW, LPW, T>(rows, slots, e0, cnt, wave, lane);
-        __syncthreads();  // every row has landed
+    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x)
+        rows_tile<W, SPW, SCALED, T>(rows, out, slot, groups, head, tile, inv_w, wave, lane);
+}
 
-        const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + e0, (uint32_t)(cnt * 16));
-        for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += NT) {
-            f4 acc = rows[0][t];
-#pragma unroll
-            for (int q = 1; q < W; ++q)
-                acc = acc + rows[q][t];  // ascending slot order, one rounding per add
-            if constexpr (SCALED)
-                acc = acc * inv_w;  // one rounding of the finished sum
-            bstore<Aux<kStream>::store>(acc, ro, t * 16u);
-        }
-        __syncthreads();  // the rows are refilled only after every thread has read them
-    }
+// Many stacked folds of one width in one launch (fold_ranks_batch): job j
+// owns workgroups [tile0_j, tile0_{j+1}), one tile each, and its first
+// workgroup also folds the job's head and tail elements.  Within a job
+// everything is k_fold_rows's, so every element's chain is the same.
+template <int W, int SPW, bool SCALED>
+__global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_batch(BatchArgs a)
+{
+    constexpr int T = RowsShape<W, SPW>::T;
+    __shared__ f4 rows[W][T];
+    int j = 0;  // the last job that starts at or before this workgroup
+    for (int k = 1; k < a.count; ++k)
+        if ((int64_t)blockIdx.x >= a.job[k].tile0)
+            j = k;
+    float *const out = a.job[j].out;
+    const int64_t len = a.job[j].len, head = a.job[j].head;
+    const StrideSlots slots{a.job[j].s0, len};
+    const int64_t tile = (int64_t)blockIdx.x - a.job[j].tile0;
+    if (tile == 0)
+        rows_edges<W, SCALED>(out, slots, len, head, threadIdx.x, a.inv_w);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rows_tile<W, SPW, SCALED, T>(rows, out, slots, (len - head) >> 2, head, tile, a.inv_w, wave, lane);
 }
 
 // Fold and write back (the fused one-device round, W <= 16 separate
@@ -374,7 +433,7 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;
-        stream_rows<W, SPW, LPW, T>(rows, slots, e0, cnt, wave, lane);
+        stream_rows<W, SPW, LPW, T>(rows, TableSlots{slots}, e0, cnt, wave, lane);
         __syncthreads();  // every row has landed
 
         for (uint32_t t = threadIdx.x; t < (uint32_t)cnt; t += NT) {
@@ -681,6 +740,30 @@ rows_kernel_t pick_rows(int32_t w, int spw)
     }
 }
 
+typedef void (*rows_batch_kernel_t)(BatchArgs);
+
+template <bool SCALED>
+rows_batch_kernel_t pick_rows_batch(int32_t w, int spw)
+{
+    switch (w) {
+    case 2: return k_fold_rows_batch<2, 1, SCALED>;
+    case 3: return k_fold_rows_batch<3, 1, SCALED>;
+    case 4: return k_fold_rows_batch<4, 1, SCALED>;
+    case 5: return spw == 2 ? k_fold_rows_batch<5, 2, SCALED> : k_fold_rows_batch<5, 1, SCALED>;
+    case 6: return spw == 2 ? k_fold_rows_batch<6, 2, SCALED> : k_fold_rows_batch<6, 1, SCALED>;
+    case 7: return spw == 2 ? k_fold_rows_batch<7, 2, SCALED> : k_fold_rows_batch<7, 1, SCALED>;
+    case 8: return spw == 2 ? k_fold_rows_batch<8, 2, SCALED> : k_fold_rows_batch<8, 1, SCALED>;
+    case 9: return spw == 2 ? k_fold_rows_batch<9, 2, SCALED> : k_fold_rows_batch<9, 1, SCALED>;
+    case 10: return spw == 2 ? k_fold_rows_batch<10, 2, SCALED> : k_fold_rows_batch<10, 1, SCALED>;
+    case 11: return spw == 2 ? k_fold_rows_batch<11, 2, SCALED> : k_fold_rows_batch<11, 1, SCALED>;
+    case 12: return spw == 2 ? k_fold_rows_batch<12, 2, SCALED> : k_fold_rows_batch<12, 1, SCALED>;
+    case 13: return spw == 2 ? k_fold_rows_batch<13, 2, SCALED> : k_fold_rows_batch<13, 1, SCALED>;
+    case 14: return spw == 2 ? k_fold_rows_batch<14, 2, SCALED> : k_fold_rows_batch<14, 1, SCALED>;
+    case 15: return spw == 2 ? k_fold_rows_batch<15, 2, SCALED> : k_fold_rows_batch<15, 1, SCALED>;
+    default: return spw == 2 ? k_fold_rows_batch<16, 2, SCALED> : k_fold_rows_batch<16, 1, SCALED>;
+    }
+}
+
 typedef void (*rows_all_kernel_t)(SlotTable, int64_t, int64_t);
 
 rows_all_kernel_t pick_rows_all(int32_t w, int spw)
@@ -793,6 +876,21 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
         e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done, begin);
     }
     return e == hipSuccess ? DETFOLD_OK : DETFOLD_ELAUNCH;
+}
+
+// The batched fold's launch (2 <= W <= 16): one workgroup per tile of every job.
+int launch_batch(const BatchArgs &a, int32_t w, const detfold_plan &p, bool scaled, void *stream)
+{
+    if (p.path != DETFOLD_PATH_ROWS || w < 2 || w > kMaxRowsW || a.count < 1 || a.count > kMaxJobs)
+        return DETFOLD_EINVAL;
+    const int spw = rows_spw(w, p.block / 64);  // the plan's workgroup size names the shape
+    rows_batch_kernel_t k = scaled ? pick_rows_batch<true>(w, spw) : pick_rows_batch<false>(w, spw);
+    BatchArgs copy = a;
+    void *args[] = {&copy};
+    return launch(reinterpret_cast<const void *>(k), dim3((unsigned)p.grid), dim3((unsigned)p.block), args,
+                  static_cast<hipStream_t>(stream), nullptr) == hipSuccess
+               ? DETFOLD_OK
+               : DETFOLD_ELAUNCH;
 }
 
 // The fused round's launch: the plan of a fold over the slot table (row

@@ -100,6 +100,22 @@ struct SlotTable {
     const float *p[kMaxRowsW];
 };
 
+// Kernel arguments of the batched fold: the jobs with at least one element,
+// in the caller's order; job j owns workgroups [tile0_j, tile0_{j+1}).
+constexpr int kMaxJobs = DETFOLD_MAX_JOBS;
+struct BatchJob {
+    float *out;
+    const float *s0;  // slot 0; slot r at s0 + r*len
+    int64_t len;
+    int64_t head;     // elements before out's first 16-byte boundary
+    int64_t tile0;    // the job's first workgroup
+};
+struct BatchArgs {
+    BatchJob job[kMaxJobs];
+    int32_t count;
+    float inv_w;
+};
+
 // Kernel arguments of the one-shot all-reduce.
 struct OneShotArgs {
     float *x[2];      // the ranks' partials, folded in place
@@ -153,6 +169,11 @@ Geometry ranks_geometry(uintptr_t out, uintptr_t stacked, int32_t W, int64_t len
 Geometry into_geometry(uintptr_t dst, uintptr_t stage, int64_t n);
 Geometry slots_geometry(const float *out, const float *const *slots, int32_t W, int64_t len);
 int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length);
+int check_batch_args(const detfold_fold_job *jobs, int32_t count, int32_t W);
+// The batched fold's kernel arguments and plan (2 <= W <= 16, arguments
+// checked): jobs without elements are dropped; a.count == 0 when none is left.
+int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t cu_count,
+               BatchArgs *a, detfold_plan *p);
 int check_round_args(float *const *arenas, int32_t W, int64_t n, const float *stage,
                      int64_t stage_elems, int32_t flags);
 int check_pair_args(const detfold_pair_link *k, const float *x0, const float *x1, int64_t n);
@@ -174,6 +195,8 @@ int launch_copy(float *const *dsts, int ndst, const float *src, int64_t len, int
 // Every slot of a table geometry becomes the fold of all (the fused round);
 // `p` is the plan make_plan gives that geometry.
 int launch_rows_all(const Geometry &g, const detfold_plan &p, void *stream);
+// The batched fold (k_fold_rows_batch); `p` from plan_batch.
+int launch_batch(const BatchArgs &a, int32_t w, const detfold_plan &p, bool scaled, void *stream);
 int launch_one_shot(const OneShotArgs &a, int nranks, void *stream);
 // The current device's address of the library's static stage
 // (DETFOLD_STATIC_STAGE_FLOATS floats), or DETFOLD_EDEVICE.

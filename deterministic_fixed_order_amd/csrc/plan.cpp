@@ -281,6 +281,79 @@ int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length)
     return DETFOLD_OK;
 }
 
+// Each job as fold_ranks checks it, and no job's output may touch another
+// job's output or arena (the workgroups of one launch run in any order).
+int check_batch_args(const detfold_fold_job *jobs, int32_t count, int32_t W)
+{
+    if (count < 0 || count > kMaxJobs || W < 1 || (count > 0 && !jobs))
+        return DETFOLD_EINVAL;
+    for (int32_t j = 0; j < count; ++j) {
+        const int rc = check_ranks_args(jobs[j].out, jobs[j].stacked, W, jobs[j].len);
+        if (rc != DETFOLD_OK)
+            return rc;
+    }
+    for (int32_t j = 0; j < count; ++j) {
+        if (jobs[j].len == 0)
+            continue;
+        const uint64_t ob = (uint64_t)jobs[j].len * 4;
+        for (int32_t k = 0; k < count; ++k) {
+            if (k == j || jobs[k].len == 0)
+                continue;
+            const uint64_t kb = (uint64_t)jobs[k].len * 4;
+            if (ranges_overlap((uintptr_t)jobs[j].out, ob, (uintptr_t)jobs[k].out, kb) ||
+                ranges_overlap((uintptr_t)jobs[j].out, ob, (uintptr_t)jobs[k].stacked, kb * (uint64_t)W))
+                return DETFOLD_EOVERLAP;
+        }
+    }
+    return DETFOLD_OK;
+}
+
+// The shape is the one the longest job would get alone (every shape gives
+// the same bits); each job takes ceil(groups / tile) workgroups, at least one
+// (for its head and tail elements).
+int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t cu_count,
+               BatchArgs *a, detfold_plan *p)
+{
+    if (W < 2 || W > kMaxRowsW || cu_count < 1)
+        return DETFOLD_EINVAL;
+    *a = BatchArgs{};
+    int32_t longest = -1;
+    for (int32_t j = 0; j < count; ++j)
+        if (jobs[j].len > 0 && (longest < 0 || jobs[j].len > jobs[longest].len))
+            longest = j;
+    *p = detfold_plan{};
+    p->path = DETFOLD_PATH_ROWS;
+    p->policy = DETFOLD_POLICY_STREAM;
+    p->unroll = 1;
+    if (longest < 0)
+        return DETFOLD_OK;  // nothing to fold
+    const Geometry lg = ranks_geometry((uintptr_t)jobs[longest].out, (uintptr_t)jobs[longest].stacked, W,
+                                       jobs[longest].len);
+    p->block = rows_block(lg);
+    p->tile = rows_tile(lg);
+    int64_t tiles = 0;
+    for (int32_t j = 0; j < count; ++j) {
+        if (jobs[j].len == 0)
+            continue;
+        BatchJob &b = a->job[a->count++];
+        b.out = jobs[j].out;
+        b.s0 = jobs[j].stacked;
+        b.len = jobs[j].len;
+        b.head = (4 - phase16((uintptr_t)jobs[j].out)) & 3;
+        if (b.head > b.len)
+            b.head = b.len;
+        b.tile0 = tiles;
+        const int64_t groups = (b.len - b.head) >> 2;
+        const int64_t t = (groups + p->tile - 1) / p->tile;
+        tiles += t > 0 ? t : 1;
+        p->body += groups;
+    }
+    if (tiles > 0x7FFFFFFF)
+        return DETFOLD_EINVAL;
+    p->grid = tiles;
+    return DETFOLD_OK;
+}
+
 int check_round_args(float *const *arenas, int32_t W, int64_t n, const float *stage,
                      int64_t stage_elems, int32_t flags)
 {

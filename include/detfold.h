@@ -128,6 +128,40 @@ int fold_slots_scaled(float *out, const float *const *slots, int32_t W, int64_t 
                       void *stream);
 
 /*
+ * fold_ranks_batch -- many stacked folds of one width in one launch: for each
+ * job j, jobs[j].out = fold_ranks of jobs[j].stacked ([W][jobs[j].len]), bit
+ * for bit what `count` separate fold_ranks calls would write.
+ *
+ * On one device the W owners of the transport dataflow each fold their own
+ * shard (mamba-rs src/dist/reducer.rs, reduce_sum_fixed_order_nccl and
+ * LoopbackWorld::run_round); one launch over all the owners' shards keeps the
+ * whole device busy where one owner's shard alone is too small to (a shard of
+ * a 40 MB arena is a wave or two of workgroups).  The same holds for any set
+ * of buffers of equal width, such as the buckets of one reduction.
+ *   jobs     HOST array of `count` jobs (copied into the launch; reusable as
+ *            soon as the call returns); a job with len == 0 is skipped
+ *   count    0 <= count <= DETFOLD_MAX_JOBS
+ *   W        >= 1, shared by every job.  2 <= W <= 16 is one launch; W = 1
+ *            and W > 16 run one launch per job.
+ * Every job is checked as fold_ranks checks its arguments; besides, no job's
+ * output may overlap another job's output or arena (DETFOLD_EOVERLAP).
+ * Arenas may overlap each other (they are only read).
+ * Errors: DETFOLD_EINVAL (also for count out of range or NULL jobs with
+ * count > 0), DETFOLD_EOVERLAP, DETFOLD_EDEVICE, DETFOLD_ELAUNCH.
+ */
+#define DETFOLD_MAX_JOBS 32
+typedef struct detfold_fold_job {
+    float *out;           /* device, len floats, written */
+    const float *stacked; /* device, [W][len] floats, read */
+    int64_t len;          /* elements per slot, >= 0 */
+} detfold_fold_job;
+int fold_ranks_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, void *stream);
+
+/* fold_ranks_batch followed by one binary32 multiply of every sum by inv_w. */
+int fold_ranks_batch_scaled(const detfold_fold_job *jobs, int32_t count, int32_t W, float inv_w,
+                            void *stream);
+
+/*
  * detfold_loopback_round -- one fixed-order reduction round across W arenas on
  * one device: afterwards every arena holds, bit for bit, the ascending-rank
  * fold of the W arenas' original contents.
@@ -324,7 +358,7 @@ int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 8
+#define DETFOLD_ABI_VERSION 9
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -408,6 +442,12 @@ typedef struct detfold_plan {
  */
 int detfold_plan_fold_ranks(uintptr_t out, uintptr_t stacked, int32_t W, int64_t len,
                             int32_t cu_count, const detfold_launch *launch, detfold_plan *plan);
+
+/* The plan of fold_ranks_batch's one launch for 2 <= W <= 16 (host only, as
+ * above): block and tile of the shape, grid = the workgroups of all jobs,
+ * body = their 16-byte groups.  With no element to fold the grid is 0. */
+int detfold_plan_fold_ranks_batch(const detfold_fold_job *jobs, int32_t count, int32_t W,
+                                  int32_t cu_count, detfold_plan *plan);
 
 /* The plan fold_into would use (host only, as above). */
 int detfold_plan_fold_into(uintptr_t dst, uintptr_t stage, int64_t n, int32_t cu_count,

@@ -47,7 +47,7 @@ def test_library_exports_nothing_but_the_c_abi(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 8
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 9
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -504,3 +504,76 @@ def test_static_round_rejects_before_any_device_work(detfold_lib):
     assert lib.detfold_loopback_round_static(_ptrs(*ar[:1]), 1, 10 ** 9, 0, None) == OK  # one rank
     assert lib.detfold_loopback_round_static(_ptrs(*ar), 4, 0, 0, None) == OK            # empty
     assert "static stage" in detfold_lib.strerror(ESIZE)
+
+
+# --------------------------------------------------------------------------
+# the batched fold: argument checks and its one-launch plan
+
+def _jobs(detfold_lib, *jobs):
+    arr = (detfold_lib.FoldJob * max(len(jobs), 1))()
+    for j, (o, st, n) in enumerate(jobs):
+        arr[j].out, arr[j].stacked, arr[j].len = o, st, n
+    return arr
+
+
+def test_batch_rejects_bad_arguments(detfold_lib):
+    df = detfold_lib
+    lib = df.load()
+    EINVAL, EOVERLAP, OK = df.EINVAL, df.EOVERLAP, df.OK
+    M = 1 << 24  # bytes between fake buffers
+    o = [BASE + k * M for k in range(4)]
+    st = [BASE + (1 << 32) + k * 16 * M for k in range(4)]
+    good = _jobs(df, (o[0], st[0], 1000), (o[1], st[1], 1000))
+    assert lib.fold_ranks_batch(good, 2, 0, None) == EINVAL                        # W < 1
+    assert lib.fold_ranks_batch(good, -1, 4, None) == EINVAL
+    assert lib.fold_ranks_batch(good, df.MAX_JOBS + 1, 4, None) == EINVAL        # too many jobs
+    assert lib.fold_ranks_batch(None, 2, 4, None) == EINVAL
+    assert lib.fold_ranks_batch(None, 0, 4, None) == OK                          # nothing to do
+    assert lib.fold_ranks_batch(_jobs(df, (o[0], st[0], 0), (0, 0, 0)), 2, 4, None) == OK
+    assert lib.fold_ranks_batch(_jobs(df, (o[0], st[0], -1)), 1, 4, None) == EINVAL
+    assert lib.fold_ranks_batch(_jobs(df, (o[0] + 2, st[0], 16)), 1, 4, None) == EINVAL   # misaligned
+    assert lib.fold_ranks_batch(_jobs(df, (0, st[0], 16)), 1, 4, None) == EINVAL          # NULL out
+    assert lib.fold_ranks_batch(_jobs(df, (st[0] + 64, st[0], 1000)), 1, 4, None) == EOVERLAP  # own arena
+    # one job's output inside another job's output or arena
+    assert lib.fold_ranks_batch(_jobs(df, (o[0], st[0], 1000), (o[0] + 3996, st[1], 1000)), 2, 4,
+                                None) == EOVERLAP
+    assert lib.fold_ranks_batch(_jobs(df, (o[0], st[0], 1000), (st[0] + 8000, st[1], 1000)), 2, 4,
+                                None) == EOVERLAP
+    # adjacent outputs, and arenas shared between jobs, are fine to plan
+    p = df.plan_fold_ranks_batch([(o[0], st[0], 1000), (o[0] + 4000, st[0], 1000)], 4, 256)
+    assert p["grid"] >= 2
+    assert lib.fold_ranks_batch_scaled(good, 2, 0, ctypes.c_float(0.5), None) == EINVAL
+
+
+def test_batch_plan_covers_every_job(detfold_lib):
+    df = detfold_lib
+    # the owner shards of a W=16 arena of 10,000,019: 3 x 625,002 and 13 x 625,001 per
+    # owner, each gathered into its own [16][l_p] scratch, written at the owners' offsets
+    shards = df.shard_plan(10_000_019, 16)
+    out = BASE
+    scratch = BASE + (1 << 34)
+    jobs, s_addr = [], scratch
+    for s, ln in shards:
+        jobs.append((out + 4 * s, s_addr, ln))
+        s_addr += 16 * ln * 4 + 4096
+    p = df.plan_fold_ranks_batch(jobs, 16, 256)
+    assert p["path"] == df.PATH_ROWS
+    # the shape is the one the longest shard would get alone
+    alone = df.plan_fold_ranks(jobs[0][0], jobs[0][1], 16, jobs[0][2], 256)
+    assert p["block"] == alone["block"] and p["tile"] == alone["tile"]
+    want_grid, want_body = 0, 0
+    for o, _, ln in jobs:
+        head = min((4 - (o // 4) % 4) % 4, ln)
+        groups = (ln - head) // 4
+        want_grid += max(1, -(-groups // p["tile"]))
+        want_body += groups
+    assert p["grid"] == want_grid and p["body"] == want_body
+    # an element-less job takes no workgroup; a job of 1..3 elements takes one
+    q = df.plan_fold_ranks_batch([(BASE, scratch, 0), (BASE + 64, scratch + 4096, 3),
+                                  (BASE + 4096, scratch + 8192, 5)], 4, 256)
+    assert q["grid"] == 2
+    assert df.plan_fold_ranks_batch([(BASE, scratch, 0)], 4, 256)["grid"] == 0
+    with pytest.raises(df.DetfoldError):
+        df.plan_fold_ranks_batch([(BASE, scratch, 10)], 1, 256)   # one launch needs 2 <= W <= 16
+    with pytest.raises(df.DetfoldError):
+        df.plan_fold_ranks_batch([(BASE, scratch, 10)], 17, 256)
