@@ -538,14 +538,16 @@ def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
 
 def plan_kernel_name(df, p, W, scaled) -> str:
     """The kernel instance a host plan names: the row bodies by slots per wave
-    (W over the plan's waves, rounded up), the wide body by its pass shape."""
+    (W over the plan's waves, rounded up) and XCD tile group, the wide body by
+    its pass shape."""
     if p["path"] == df.PATH_ROWS and W > 16:
         shape = "16,1,4" if p["block"] == 1024 else "8,2,1"  # waves, slots per wave, KiB
         return "k_fold_rows_wide<%s,%s> grid=%d block=%d tile=%d" % (
             shape, str(scaled).lower(), p["grid"], p["block"], p["tile"])
     if p["path"] == df.PATH_ROWS:
-        return "k_fold_rows<%d,%d,%s> grid=%d block=%d tile=%d" % (
-            W, -(-W // (p["block"] // 64)), str(scaled).lower(), p["grid"], p["block"], p["tile"])
+        return "k_fold_rows<%d,%d,%s> grid=%d block=%d tile=%d xcd_group=%d" % (
+            W, -(-W // (p["block"] // 64)), str(scaled).lower(), p["grid"], p["block"], p["tile"],
+            p.get("group", 1))
     body = "k_fold_vector" if p["path"] == df.PATH_VECTOR else "k_fold_scalar"
     ws = W if W in (1, 2, 4, 8, 16) else 0
     pol = 1 if p["policy"] == df.POLICY_STREAM else 0
@@ -770,11 +772,14 @@ def bench_round(args, torch, df, dev):
 
 def bench_pair(args, torch, df, dev):
     """Two ranks on two streams: one all-reduce per call (push, event, fold on
-    both ranks), back-to-back, and one call with a host synchronization."""
+    both ranks), back-to-back through the binding, one call with a host
+    synchronization, and the device time per call (calls queued behind a
+    spin kernel, so the host's enqueue cost is out of the measurement)."""
     import fold_inputs
 
     link = df.PairLink(max(JOIN_SIZES), device=dev)
     shot = df.OneShotLink(max(JOIN_SIZES), device=dev, stream=torch.cuda.Stream(device=dev))
+    cycles_per_ms = sleep_cycles_per_ms(torch)
     rows = []
     for n in JOIN_SIZES:
         xa = torch.from_numpy(fold_inputs.vecf(n, 11 + n)).to(dev)
@@ -797,11 +802,13 @@ def bench_pair(args, torch, df, dev):
                 st.synchronize()
             one.append((time.perf_counter() - t1) * 1e6)
         row = {"n": n, "back_to_back_us_per_call": round(b2b, 3),
-               "enqueue_to_complete_us_median": round(statistics.median(one), 3)}
+               "enqueue_to_complete_us_median": round(statistics.median(one), 3),
+               "device_us_per_call": round(pair_device_us(torch, link, xa, xb, cycles_per_ms), 3)}
         row["one_shot"] = bench_one_shot(torch, df, dev, shot, xa, xb)
         rows.append(row)
-        log("pair all-reduce n=%6d: %.2f us/call back-to-back, %.2f us call+sync; one-shot %s"
-            % (n, b2b, statistics.median(one), row["one_shot"]))
+        log("pair all-reduce n=%6d: %.2f us/call back-to-back, %.2f us call+sync, %.2f us/call on the "
+            "device; one-shot %s" % (n, b2b, statistics.median(one), row["device_us_per_call"],
+                                      row["one_shot"]))
     words = shot.barrier_words()
     if words != [0, 0]:
         raise RuntimeError("one-shot barrier words %s after the sweep" % words)
@@ -814,6 +821,40 @@ def bench_pair(args, torch, df, dev):
         "data": "synthetic", "config": {"workload": WORKLOAD_NAMES["pair"], "n": 4096},
         "pair": rows,
     }
+
+
+def sleep_cycles_per_ms(torch) -> float:
+    """Cycles of torch's bounded device spin (torch.cuda._sleep) per ms."""
+    probe = 1 << 22
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    torch.cuda._sleep(probe)
+    t1.record()
+    t1.synchronize()
+    return probe / t0.elapsed_time(t1)
+
+
+def pair_device_us(torch, link, xa, xb, cycles_per_ms, calls=100, hold_ms=20.0):
+    """Device time per pair all-reduce, without the host: `calls` calls are
+    enqueued while a bounded spin kernel holds the current stream (every call
+    forks from it), so they run back to back once it ends; events on the
+    current stream after the spin and after the last call's join bracket
+    them.  (The link cannot be captured into a graph.)"""
+    cur = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * cycles_per_ms))
+    start.record(cur)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        link.all_reduce(xa, xb)
+    enqueue_ms = (time.perf_counter() - t0) * 1e3
+    end.record(cur)
+    end.synchronize()
+    if enqueue_ms > hold_ms:
+        log("pair device time: enqueueing %d calls took %.1f ms, longer than the %.1f ms hold"
+            % (calls, enqueue_ms, hold_ms))
+    return start.elapsed_time(end) * 1e3 / calls
 
 
 def bench_one_shot(torch, df, dev, shot, xa, xb):

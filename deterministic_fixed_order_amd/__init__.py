@@ -31,10 +31,10 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdetfold.so")
 
-OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE, ESIZE = 0, 1, 2, 3, 4, 5
+OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE, ESIZE, ECAPTURE = 0, 1, 2, 3, 4, 5, 6
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 9
+ABI_VERSION = 11
 STATIC_STAGE_FLOATS = 1 << 22
 ONE_SHOT_BLOCKS = 64
 ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
@@ -61,7 +61,8 @@ class DetfoldError(RuntimeError):
 
 class Launch(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32), ("policy", ctypes.c_int32)]
+                ("grid", ctypes.c_int64), ("unroll", ctypes.c_int32), ("policy", ctypes.c_int32),
+                ("group", ctypes.c_int32)]
 
 
 class FoldJob(ctypes.Structure):
@@ -83,7 +84,8 @@ class OneShotLinkC(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("unroll", ctypes.c_int32), ("head", ctypes.c_int32), ("tail", ctypes.c_int32),
-                ("policy", ctypes.c_int32), ("body", ctypes.c_int64), ("tile", ctypes.c_int64)]
+                ("policy", ctypes.c_int32), ("body", ctypes.c_int64), ("tile", ctypes.c_int64),
+                ("group", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -254,12 +256,12 @@ def fold_ranks_batch(outs, stackeds, inv_w: Optional[float] = None, stream=None)
 
 
 def fold_ranks_ex(out, stacked, *, scaled: bool = False, inv_w: float = 1.0, path: int = 0,
-                  block: int = 0, grid: int = 0, unroll: int = 0, policy: int = 0,
+                  block: int = 0, grid: int = 0, unroll: int = 0, policy: int = 0, group: int = 0,
                   stream=None) -> None:
     """``fold_ranks`` / ``fold_ranks_scaled`` with an explicit launch override
     (tests and tuning sweeps only)."""
     W, n = _stacked_shape(out, stacked)
-    cfg = Launch(path, block, grid, unroll, policy)
+    cfg = Launch(path, block, grid, unroll, policy, group)
     _check(load().detfold_fold_ranks_ex(out.data_ptr(), stacked.data_ptr(), W, n, int(scaled),
                                         float(inv_w), ctypes.byref(cfg),
                                         _stream_handle(out, stream)), "detfold_fold_ranks_ex")
@@ -370,7 +372,18 @@ def loopback_round_static(arenas, *, reverse_delivery: bool = False, stream=None
 class PairLink:
     """Two ranks on one device, each a stream, joined by staging buffers and
     events (the library's ``detfold_pair_link``).  ``all_reduce(x0, x1)`` leaves
-    ``x0 + x1`` in both, folded on each rank's own stream."""
+    ``x0 + x1`` in both, folded on each rank's own stream.
+
+    Stream order: every call first makes both rank streams wait for the
+    caller's current stream (so work already queued there on the tensors,
+    such as the writes that produced them, comes first), and before it
+    returns makes the current stream wait for both rank streams (so later
+    work there, including the allocator's reuse of a freed tensor, comes
+    after).  Between the two the ranks run on their own streams.
+
+    The link cannot be captured into a HIP graph (the library returns
+    ``ECAPTURE``); every call raises before touching the device while the
+    current stream is capturing."""
 
     def __init__(self, capacity: int, device=None, streams=None):
         import torch
@@ -394,13 +407,28 @@ class PairLink:
         self._c.capacity = capacity
         _check(load().detfold_pair_link_init(ctypes.byref(self._c)), "pair_link_init")
 
+    def _fork(self):
+        import torch
+        if torch.cuda.is_current_stream_capturing():
+            raise DetfoldError(ECAPTURE, "PairLink")
+        cur = torch.cuda.current_stream(self.device)
+        for s in self.streams:
+            s.wait_stream(cur)
+        return cur
+
+    def _join(self, cur) -> None:
+        for s in self.streams:
+            cur.wait_stream(s)
+
     def all_reduce(self, x0, x1) -> None:
         _f32_device(x0, "x0")
         _f32_device(x1, "x1")
         if x0.numel() != x1.numel():
             raise ValueError("x0 has %d elements, x1 %d" % (x0.numel(), x1.numel()))
+        cur = self._fork()
         _check(load().detfold_pair_all_reduce(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
                                               x0.numel()), "pair_all_reduce")
+        self._join(cur)
 
     def broadcast(self, root: int, src, dst) -> None:
         """``dst`` (rank ``1 - root``) becomes a byte copy of ``src`` (rank ``root``)."""
@@ -408,8 +436,10 @@ class PairLink:
         _f32_device(dst, "dst")
         if src.numel() != dst.numel():
             raise ValueError("src has %d elements, dst %d" % (src.numel(), dst.numel()))
+        cur = self._fork()
         _check(load().detfold_pair_broadcast(ctypes.byref(self._c), int(root), src.data_ptr(),
                                              dst.data_ptr(), src.numel()), "pair_broadcast")
+        self._join(cur)
 
     def all_gather(self, x0, x1, f0, f1) -> None:
         """``f0`` and ``f1`` (2 * span floats) both become ``[x0 | x1]``."""
@@ -418,8 +448,10 @@ class PairLink:
         span = x0.numel()
         if x1.numel() != span or f0.numel() != 2 * span or f1.numel() != 2 * span:
             raise ValueError("all_gather needs x0, x1 of one span and f0, f1 of twice it")
+        cur = self._fork()
         _check(load().detfold_pair_all_gather(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
                                               f0.data_ptr(), f1.data_ptr(), span), "pair_all_gather")
+        self._join(cur)
 
 
 class OneShotLink:
@@ -472,14 +504,25 @@ class OneShotLink:
         _check(load().detfold_one_shot_init(ctypes.byref(self._c)), "one_shot_init")
 
     def all_reduce(self, x0, x1) -> None:
+        """Both ranks in one launch on the link's stream, ordered after the
+        caller's current stream and before its later work (as PairLink)."""
+        import torch
         _f32_device(x0, "x0")
         _f32_device(x1, "x1")
         if x0.numel() != x1.numel():
             raise ValueError("x0 has %d elements, x1 %d" % (x0.numel(), x1.numel()))
+        cur = torch.cuda.current_stream(self.device)
+        other = cur.cuda_stream != self.stream.cuda_stream
+        if other:
+            self.stream.wait_stream(cur)
         _check(load().detfold_one_shot_all_reduce(ctypes.byref(self._c), x0.data_ptr(),
                                                   x1.data_ptr(), x0.numel()), "one_shot_all_reduce")
+        if other:
+            cur.wait_stream(self.stream)
 
     def rank(self, r: int, x, stream=None) -> None:
+        """Rank r's kernel alone, on ``stream`` (default: the caller's current
+        stream); the caller orders it against other streams."""
         _f32_device(x, "x")
         _check(load().detfold_one_shot_rank(ctypes.byref(self._c), int(r), x.data_ptr(), x.numel(),
                                             _stream_handle(x, stream)), "one_shot_rank")

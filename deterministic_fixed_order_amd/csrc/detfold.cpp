@@ -166,11 +166,26 @@ int run_round(float *const *arenas, int32_t W, int64_t n, float *stage, int32_t 
 // folds in place.  Ordering is by events on the streams only -- no device
 // flag, no spin -- so neither rank's kernel ever waits on the other's.
 
+// The pair link's launches have their dispatch record the link's events
+// (hipExtLaunchKernel), which is not a form stream capture takes: refuse a
+// link whose streams are being captured, before any work is enqueued.
+int link_not_capturing(const detfold_pair_link *k)
+{
+    for (int r = 0; r < 2; ++r) {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(static_cast<hipStream_t>(k->stream[r]), &st) != hipSuccess)
+            return DETFOLD_ELAUNCH;
+        if (st != hipStreamCaptureStatusNone)
+            return DETFOLD_ECAPTURE;
+    }
+    return DETFOLD_OK;
+}
+
 int run_pair(const detfold_pair_link *k, float *x0, float *x1, int64_t n)
 {
     int32_t cu = 0;
     int rc = current_cu_count(&cu);
-    if (rc != DETFOLD_OK)
+    if (rc != DETFOLD_OK || (rc = link_not_capturing(k)) != DETFOLD_OK)
         return rc;
     float *x[2] = {x0, x1};
     hipStream_t st[2] = {static_cast<hipStream_t>(k->stream[0]), static_cast<hipStream_t>(k->stream[1])};
@@ -202,7 +217,7 @@ int run_broadcast(const detfold_pair_link *k, int32_t root, const float *src, fl
 {
     int32_t cu = 0;
     int rc = current_cu_count(&cu);
-    if (rc != DETFOLD_OK)
+    if (rc != DETFOLD_OK || (rc = link_not_capturing(k)) != DETFOLD_OK)
         return rc;
     const int32_t o = 1 - root;
     hipStream_t sr = static_cast<hipStream_t>(k->stream[root]);
@@ -225,7 +240,7 @@ int run_all_gather(const detfold_pair_link *k, const float *x0, const float *x1,
 {
     int32_t cu = 0;
     int rc = current_cu_count(&cu);
-    if (rc != DETFOLD_OK)
+    if (rc != DETFOLD_OK || (rc = link_not_capturing(k)) != DETFOLD_OK)
         return rc;
     const float *x[2] = {x0, x1};
     float *f[2] = {f0, f1};
@@ -365,6 +380,8 @@ const char *detfold_strerror(int rc)
     case DETFOLD_EDEVICE: return "no usable current HIP device";
     case DETFOLD_ESIZE: return "request exceeds the library's static stage "
                                "(DETFOLD_STATIC_STAGE_FLOATS floats)";
+    case DETFOLD_ECAPTURE: return "the pair link's streams are being captured into a graph, "
+                                  "which the pair link does not support";
     default: return "unknown detfold return code";
     }
 }

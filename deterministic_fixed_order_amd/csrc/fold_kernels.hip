@@ -311,6 +311,28 @@ __device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const Slots &slot,
     }
 }
 
+// The tile workgroup b folds when each XCD is to take runs of `group`
+// neighbouring tiles.  Workgroups go to the 8 XCDs round-robin (b mod 8), so
+// within each block of 8*group workgroups XCD x gets tiles x*group ..
+// x*group+group-1; a last, partial block keeps b.  A 16-byte run of a slot
+// that does not start on a 128-byte line shares its first and last line with
+// the neighbouring tiles' runs; on one XCD that line is fetched once into its
+// L2, across XCDs once per XCD.  Any group gives a permutation of the tiles,
+// so the bits never depend on it.  group is a power of two (the plan and the
+// override check see to it), so the index arithmetic is shifts and masks.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles, int group)
+{
+    static_assert(kXcds == 8, "three bits of XCD index");
+    if (group <= 1)
+        return b;
+    const int lg = __builtin_ctz((unsigned)group);
+    const int64_t span = (int64_t)kXcds << lg;
+    if (b >= (ntiles & ~(span - 1)))
+        return b;
+    const int64_t r = b & (span - 1);
+    return b - r + ((r & (kXcds - 1)) << lg) + (r >> 3);
+}
+
 // One tile of the row body: the W slots' bytes for groups [tile*T, tile*T+cnt)
 // of `out` streamed into the rows, then every thread folds whole groups in
 // ascending row order and stores them.  Every thread of the workgroup calls
@@ -358,16 +380,22 @@ __device__ __forceinline__ void rows_edges(float *out, const Slots &slots, int64
 
 template <int W, int SPW, bool SCALED>
 __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows(float *out, SlotTable slots, int64_t len,
-                                                            int64_t head, float inv_w)
+                                                            int64_t head, float inv_w, int group)
 {
     constexpr int T = RowsShape<W, SPW>::T;
     __shared__ f4 rows[W][T];
     const TableSlots slot{slots};
     rows_edges<W, SCALED>(out, slot, len, head, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, inv_w);
     const int64_t groups = (len - head) >> 2;
+    const int64_t ntiles = (groups + T - 1) / T;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x)
+    if ((int64_t)gridDim.x == ntiles) {  // one pass: one tile per workgroup
+        rows_tile<W, SPW, SCALED, T>(rows, out, slot, groups, head, xcd_tile(blockIdx.x, ntiles, group), inv_w,
+                                     wave, lane);
+        return;
+    }
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
         rows_tile<W, SPW, SCALED, T>(rows, out, slot, groups, head, tile, inv_w, wave, lane);
 }
 
@@ -380,14 +408,15 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_batch(Bat
 {
     constexpr int T = RowsShape<W, SPW>::T;
     __shared__ f4 rows[W][T];
-    int j = 0;  // the last job that starts at or before this workgroup
+    const int64_t b = xcd_tile(blockIdx.x, gridDim.x, a.group);
+    int j = 0;  // the last job that starts at or before workgroup b
     for (int k = 1; k < a.count; ++k)
-        if ((int64_t)blockIdx.x >= a.job[k].tile0)
+        if (b >= a.job[k].tile0)
             j = k;
     float *const out = a.job[j].out;
     const int64_t len = a.job[j].len, head = a.job[j].head;
     const StrideSlots slots{a.job[j].s0, len};
-    const int64_t tile = (int64_t)blockIdx.x - a.job[j].tile0;
+    const int64_t tile = b - a.job[j].tile0;
     if (tile == 0)
         rows_edges<W, SCALED>(out, slots, len, head, threadIdx.x, a.inv_w);
     const uint32_t lane = threadIdx.x & 63;
@@ -716,7 +745,7 @@ scalar_kernel_t pick_scalar_w(int unroll, int policy)
     }
 }
 
-typedef void (*rows_kernel_t)(float *, SlotTable, int64_t, int64_t, float);
+typedef void (*rows_kernel_t)(float *, SlotTable, int64_t, int64_t, float, int);
 
 template <bool SCALED>
 rows_kernel_t pick_rows(int32_t w, int spw)
@@ -862,7 +891,8 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
         SlotTable slots = {};
         for (int32_t r = 0; r < w; ++r)
             slots.p[r] = reinterpret_cast<const float *>(g.slot(r));
-        void *args[] = {&out, &slots, &len, &head, &inv_w};
+        int group = p.group;
+        void *args[] = {&out, &slots, &len, &head, &inv_w, &group};
         e = launch(reinterpret_cast<const void *>(k), grid, block, args, stream, done, begin);
     } else if (p.path == DETFOLD_PATH_VECTOR) {
         vector_kernel_t k = scaled ? pick_vector<true>(w, p.unroll, policy)

@@ -13,6 +13,8 @@
 namespace detfold_impl {
 
 constexpr int kMaxBlock = 1024;
+constexpr int kXcds = 8;           // accelerator complex dies of an MI355X; workgroups go round-robin
+constexpr int kMaxGroup = 64;      // largest XCD tile group a launch override may ask for
 constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth path
 constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
 constexpr int kMaxRowsW = 16;      // widest fold the LDS row body takes (one wave per slot)
@@ -58,6 +60,22 @@ constexpr int rows_kib_per_wave(int w)
 // The shapes differ only in which wave loads which slot; every element's
 // chain is the same.
 constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot lengths at this multiple
+
+// Stacked arenas whose slot length in bytes is not a multiple of kRepeatBytes
+// (16 MiB) -- their W slots sit at unrelated low address bits -- take, from
+// three slots up, runs of kSlotGroup neighbouring tiles per XCD, and from
+// nine slots up two slots per wave.  Measured on MI355X over 23 widths,
+// lengths and alignments (8 interleaved rounds each, every variant
+// bit-checked): +5% to +13% at every shifted arena of three to sixteen slots
+// (W=16 x 10,000,019 at base+1 element: 6,126 -> 6,514 GB/s; W=8 x 10^7 at
+// base+1: 5,845 -> 6,610), +2% to +10% on co-aligned arenas of such lengths
+// (W=8 x 6,291,456: 6,615 -> 7,279), a tie at W=4 x 10^8.  Where the slot
+// length is such a multiple (W=8 x 2^24, W=4 x 2^24, W=2 x 2^26) plain
+// round-robin stays best: groups lose up to 8% (W=8), and groups of 2 or 4
+// up to 35% at W=4.  At W=2 groups of 8 lose up to 2.5%, so two-slot folds
+// keep plain round-robin.
+constexpr int64_t kRepeatBytes = (int64_t)1 << 24;
+constexpr int kSlotGroup = 8;
 constexpr int rows_kib_per_wave(int w, int spw)
 {
     return spw == 1 ? rows_kib_per_wave(w) : 1;
@@ -113,6 +131,7 @@ struct BatchJob {
 struct BatchArgs {
     BatchJob job[kMaxJobs];
     int32_t count;
+    int32_t group;  // XCD tile group (xcd_tile) over the launch's workgroups
     float inv_w;
 };
 
@@ -154,9 +173,12 @@ inline int phase16(uintptr_t a) { return (int)((a >> 2) & 3); }
 
 // --- plan.cpp: host only, no device access ---------------------------------
 bool vector_legal(const Geometry &g);
+bool slots_repeat(const Geometry &g);
 int rows_slots_per_wave(const Geometry &g);
 int rows_block(const Geometry &g);
 int64_t rows_tile(const Geometry &g);
+int64_t rows_tile_for_block(const Geometry &g, int block);
+int rows_group(const Geometry &g, int block);
 int check_override(const detfold_launch *o);
 int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, int policy,
               detfold_plan *p);

@@ -28,17 +28,31 @@ bool vector_legal(const Geometry &g)
     return true;
 }
 
-// Slots each wave of the row body streams: for eight slots two, unless they
-// are a stacked arena whose slot length is a multiple of kOneSlotAlign; for
-// the other widths from five to sixteen two when every slot shares out's
-// 16-byte phase (an odd width's last wave streams one); one otherwise.
+// Whether the slots of a stacked arena repeat every address bit below
+// kRepeatBytes (the slot length in bytes is a multiple of it).  Separate
+// slot buffers (a table) count as repeating: the rules below were measured
+// on stacked arenas, and tables keep the shapes they had before.
+bool slots_repeat(const Geometry &g)
+{
+    return g.has_table || (g.stride * 4) % kRepeatBytes == 0;
+}
+
+// Slots each wave of the row body streams.
+//  * Stacked arenas whose slots do not repeat the low address bits: two from
+//    nine slots up, else one (with the XCD tile group of rows_group).
+//  * Otherwise: for eight slots two, unless the slot length is a multiple of
+//    kOneSlotAlign; for the other widths from five to sixteen two when every
+//    slot shares out's 16-byte phase (an odd width's last wave streams one);
+//    one otherwise.
 int rows_slots_per_wave(const Geometry &g)
 {
+    if (g.w > kMaxRowsW || g.w < 5)
+        return 1;
+    if (!slots_repeat(g))
+        return g.w >= 9 ? 2 : 1;
     if (g.w == 8)
         return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
-    if (g.w >= 5 && g.w <= kMaxRowsW)
-        return vector_legal(g) ? 2 : 1;
-    return 1;
+    return vector_legal(g) ? 2 : 1;
 }
 
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per
@@ -56,6 +70,38 @@ int64_t rows_tile(const Geometry &g)
     if (g.w <= kMaxRowsW)
         return (int64_t)rows_kib_per_wave(g.w, rows_slots_per_wave(g)) * 64;
     return (int64_t)(vector_legal(g) ? kWideAlignedKiB : kWideKiB) * 64;
+}
+
+// The tile of the row-body shape a workgroup size names, or 0 if it names
+// none: up to 16 slots, 64*W threads (one slot per wave) or, from five slots
+// up, 64*ceil(W/2) (two slots per wave); beyond 16, 64*kWideWaves or
+// 64*kWideAlignedWaves threads (the two pass shapes).  Any shape folds any
+// alignment, with the same bits; the plan picks the faster one.
+int64_t rows_tile_for_block(const Geometry &g, int block)
+{
+    if (g.w > kMaxRowsW) {
+        if (block == 64 * kWideWaves)
+            return (int64_t)kWideKiB * 64;
+        if (block == 64 * kWideAlignedWaves)
+            return (int64_t)kWideAlignedKiB * 64;
+        return 0;
+    }
+    if (block == 64 * g.w)
+        return (int64_t)rows_kib_per_wave(g.w, 1) * 64;
+    if (g.w >= 5 && block == 64 * rows_waves(g.w, 2))
+        return (int64_t)rows_kib_per_wave(g.w, 2) * 64;
+    return 0;
+}
+
+// XCD tile group of the row body (xcd_tile in fold_kernels.hip): runs of
+// kSlotGroup tiles per XCD for a stacked arena of three to sixteen slots that
+// do not repeat the low address bits, plain round-robin otherwise.
+int rows_group(const Geometry &g, int block)
+{
+    (void)block;
+    if (g.w < 3 || g.w > kMaxRowsW || slots_repeat(g))
+        return 1;
+    return kSlotGroup;
 }
 
 // Positions per thread per pass.  The vector body moves 16 bytes per slot per
@@ -80,6 +126,8 @@ int check_override(const detfold_launch *o)
         return DETFOLD_EINVAL;
     if (o->policy == DETFOLD_POLICY_CACHED && o->unroll > 1)
         return DETFOLD_EINVAL;  // the unhinted kernels exist with unroll 1 only
+    if (o->group < 0 || o->group > kMaxGroup || (o->group & (o->group - 1)))
+        return DETFOLD_EINVAL;  // 0 (the plan's choice) or a power of two up to kMaxGroup
     return DETFOLD_OK;
 }
 
@@ -101,7 +149,7 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
     int rc = check_override(ovr);
     if (rc != DETFOLD_OK)
         return rc;
-    const detfold_launch o = ovr ? *ovr : detfold_launch{DETFOLD_PATH_AUTO, 0, 0, 0, 0};
+    const detfold_launch o = ovr ? *ovr : detfold_launch{DETFOLD_PATH_AUTO, 0, 0, 0, 0, 0};
     if (o.policy)
         policy = o.policy;
 
@@ -120,7 +168,7 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
     if (path == DETFOLD_PATH_VECTOR && !vec_ok)
         return DETFOLD_EINVAL;
     if (path == DETFOLD_PATH_ROWS &&
-        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && o.block != rows_block(g)) ||
+        (!rows_ok || policy == DETFOLD_POLICY_CACHED || (o.block && !rows_tile_for_block(g, o.block)) ||
          o.unroll > 1))
         return DETFOLD_EINVAL;
 
@@ -138,10 +186,13 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
         p->body = (g.len - head) >> 2;
         p->tail = (int32_t)((g.len - head) & 3);
     }
+    p->group = 1;
     if (path == DETFOLD_PATH_ROWS) {
         p->unroll = 1;
-        p->block = rows_block(g);
-        p->tile = rows_tile(g);
+        p->block = o.block ? o.block : rows_block(g);
+        p->tile = rows_tile_for_block(g, p->block);
+        if (g.w <= kMaxRowsW)
+            p->group = o.group ? o.group : rows_group(g, p->block);
     } else {
         p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
         int block = o.block;
@@ -226,7 +277,7 @@ Geometry into_geometry(uintptr_t dst, uintptr_t stage, int64_t n)
 int plan_into(const Geometry &g, int32_t cu_count, detfold_plan *p)
 {
     if (g.len * 4 <= kLatencyBytes) {
-        const detfold_launch o = {DETFOLD_PATH_AUTO, 0, 0, 1, 0};
+        const detfold_launch o = {DETFOLD_PATH_AUTO, 0, 0, 1, 0, 0};
         return make_plan(g, cu_count, &o, DETFOLD_POLICY_CACHED, p);
     }
     return make_plan(g, cu_count, nullptr, DETFOLD_POLICY_STREAM, p);
@@ -325,12 +376,16 @@ int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t c
     p->path = DETFOLD_PATH_ROWS;
     p->policy = DETFOLD_POLICY_STREAM;
     p->unroll = 1;
+    p->group = 1;
+    a->group = 1;
     if (longest < 0)
         return DETFOLD_OK;  // nothing to fold
     const Geometry lg = ranks_geometry((uintptr_t)jobs[longest].out, (uintptr_t)jobs[longest].stacked, W,
                                        jobs[longest].len);
     p->block = rows_block(lg);
     p->tile = rows_tile(lg);
+    p->group = rows_group(lg, p->block);
+    a->group = p->group;
     int64_t tiles = 0;
     for (int32_t j = 0; j < count; ++j) {
         if (jobs[j].len == 0)

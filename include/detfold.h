@@ -53,6 +53,7 @@ extern "C" {
 #define DETFOLD_ELAUNCH 3  /* the HIP launch was refused                                 */
 #define DETFOLD_EDEVICE 4  /* no current HIP device, or its properties could not be read */
 #define DETFOLD_ESIZE 5    /* the request needs more than the library's static stage     */
+#define DETFOLD_ECAPTURE 6 /* a pair-link stream is being captured into a graph         */
 
 /*
  * fold_ranks -- out[i] = ((s_0[i] + s_1[i]) + ...) + s_{W-1}[i]
@@ -234,6 +235,10 @@ int detfold_loopback_round_static(float *const *arenas, int32_t W, int64_t n, in
  * spins on a flag, so neither rank can starve the other however much other
  * work is resident.  The caller owns every buffer, stream and event; the
  * library keeps no state between calls.
+ * The link's launches have their dispatch record the link's events, a form
+ * stream capture does not take: every pair-link call on a stream that is
+ * being captured into a graph returns DETFOLD_ECAPTURE before enqueueing
+ * anything.
  */
 typedef struct detfold_pair_link {
     void *stream[2];  /* hipStream_t of rank 0 and rank 1 (one device; may be equal) */
@@ -358,7 +363,7 @@ int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 9
+#define DETFOLD_ABI_VERSION 11
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -412,12 +417,16 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
 
 typedef struct detfold_launch {
     int32_t path;   /* DETFOLD_PATH_*; VECTOR where the alignment forbids it is EINVAL */
-    int32_t block;  /* threads per workgroup: 0 = default, else a multiple of 64 in [64, 1024]
-                       (ROWS: 0 or 64*W) */
+    int32_t block;  /* threads per workgroup: 0 = default, else a multiple of 64 in [64, 1024].
+                       ROWS names the shape: W <= 16: 64*W (one slot per wave) or, W >= 5,
+                       64*ceil(W/2) (two slots per wave); W > 16: 1024 or 512 (the pass shapes) */
     int64_t grid;   /* workgroups: 0 = one pass, else >= 1 (workgroups loop over the tiles) */
     int32_t unroll; /* groups (vector) or elements (scalar) per thread per tile: 0 = default, 1, 2 or 4
                        (ROWS: 0 or 1) */
     int32_t policy; /* DETFOLD_POLICY_*: 0 = the entry point's own policy */
+    int32_t group;  /* ROWS, W <= 16, one pass: each XCD takes runs of this many neighbouring
+                       tiles (0 = the plan's choice, else a power of two up to 64; 1 = plain
+                       round-robin) */
 } detfold_launch;
 
 typedef struct detfold_plan {
@@ -430,6 +439,7 @@ typedef struct detfold_plan {
     int32_t policy; /* DETFOLD_POLICY_STREAM or DETFOLD_POLICY_CACHED */
     int64_t body;   /* 4-element groups (rows, vector) or elements (scalar) */
     int64_t tile;   /* body positions one workgroup folds per pass */
+    int32_t group;  /* XCD tile group of the row body (1 = plain round-robin) */
 } detfold_plan;
 
 /*

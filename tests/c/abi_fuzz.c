@@ -21,8 +21,11 @@ static void fail(const char *what, int64_t w, int64_t len)
 }
 
 /* What a kernel launch needs from a plan. */
-static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coaligned)
+static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coaligned, int32_t forced_block,
+                       int32_t forced_group)
 {
+    if (p->group < 1 || p->group > 64)
+        fail("XCD group out of range", W, len);
     if (len == 0) {
         if (p->grid != 0)
             fail("empty fold with a grid", W, len);
@@ -46,8 +49,24 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
     /* eight slots of a stacked arena: two slots per wave unless len is a multiple of 2^24;
      * the other widths from five to sixteen: two when every slot shares out's 16-byte phase,
      * an odd width's last wave streaming one */
-    const int spw = W == 8 ? (len % ((int64_t)1 << 24) != 0 ? 2 : 1)
-                           : (W >= 5 && W <= 16 && coaligned) ? 2 : 1;
+    if (p->path == DETFOLD_PATH_ROWS && forced_block) {
+        /* an override names the shape: the plan keeps it, with that shape's tile */
+        const int64_t tile = W > 16 ? (forced_block == 1024 ? 256 : 64)
+                                    : forced_block == 64 * W ? 64 * (W <= 2 ? 8 : (W + 3) / 4) : 64;
+        if (p->block != forced_block || p->tile != tile)
+            fail("row body override not kept", W, len);
+        return;
+    }
+    /* slots that do not repeat the low 16 MiB of address: two slots per wave
+     * from nine up and runs of 8 tiles per XCD from three up */
+    const int repeat = len % ((int64_t)1 << 22) == 0;
+    const int spw = (W < 5 || W > 16) ? 1
+                    : !repeat ? (W >= 9 ? 2 : 1)
+                    : W == 8 ? (len % ((int64_t)1 << 24) != 0 ? 2 : 1)
+                    : coaligned ? 2 : 1;
+    if (p->path == DETFOLD_PATH_ROWS && W <= 16 &&
+        p->group != (forced_group ? forced_group : (W >= 3 && !repeat) ? 8 : 1))
+        fail("row body with the wrong XCD group", W, len);
     if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * ((W + spw - 1) / spw) : coaligned ? 512 : 1024))
         fail("row body with the wrong workgroup size", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W <= 16 && spw == 2 && p->tile != 64)
@@ -73,19 +92,25 @@ int main(void)
                                       UINTPTR_MAX - 15, UINTPTR_MAX - 3};
     static const int32_t cus[] = {-1, 0, 1, 7, 256, INT32_MAX};
     const detfold_launch overrides[] = {
-        {DETFOLD_PATH_AUTO, 0, 0, 0, DETFOLD_POLICY_DEFAULT},
-        {DETFOLD_PATH_VECTOR, 256, 7, 2, DETFOLD_POLICY_DEFAULT},
-        {DETFOLD_PATH_SCALAR, 1024, 1, 4, DETFOLD_POLICY_STREAM},
-        {DETFOLD_PATH_ROWS, 0, 3, 0, DETFOLD_POLICY_DEFAULT},
-        {DETFOLD_PATH_ROWS, 1024, 0, 1, DETFOLD_POLICY_DEFAULT},
-        {DETFOLD_PATH_AUTO, 0, 0, 0, DETFOLD_POLICY_CACHED},
-        {DETFOLD_PATH_AUTO, 64, 0x7FFFFFFF, 1, DETFOLD_POLICY_CACHED},
-        {7, 0, 0, 0, 0},
-        {DETFOLD_PATH_AUTO, 100, 0, 0, 0},
-        {DETFOLD_PATH_AUTO, 0, -1, 0, 0},
-        {DETFOLD_PATH_AUTO, 0, 0, 3, 0},
-        {DETFOLD_PATH_AUTO, 0, 0, 2, DETFOLD_POLICY_CACHED},
-        {DETFOLD_PATH_AUTO, 0, 0, 0, 9},
+        {DETFOLD_PATH_AUTO, 0, 0, 0, DETFOLD_POLICY_DEFAULT, 0},
+        {DETFOLD_PATH_VECTOR, 256, 7, 2, DETFOLD_POLICY_DEFAULT, 0},
+        {DETFOLD_PATH_SCALAR, 1024, 1, 4, DETFOLD_POLICY_STREAM, 0},
+        {DETFOLD_PATH_ROWS, 0, 3, 0, DETFOLD_POLICY_DEFAULT, 0},
+        {DETFOLD_PATH_ROWS, 1024, 0, 1, DETFOLD_POLICY_DEFAULT, 0},
+        {DETFOLD_PATH_ROWS, 512, 0, 0, DETFOLD_POLICY_DEFAULT, 4},
+        {DETFOLD_PATH_ROWS, 256, 0, 0, DETFOLD_POLICY_DEFAULT, 8},
+        {DETFOLD_PATH_ROWS, 0, 0, 0, DETFOLD_POLICY_DEFAULT, 64},
+        {DETFOLD_PATH_ROWS, 0, 0, 0, DETFOLD_POLICY_DEFAULT, 65},
+        {DETFOLD_PATH_ROWS, 0, 0, 0, DETFOLD_POLICY_DEFAULT, 12},
+        {DETFOLD_PATH_AUTO, 0, 0, 0, DETFOLD_POLICY_DEFAULT, -1},
+        {DETFOLD_PATH_AUTO, 0, 0, 0, DETFOLD_POLICY_CACHED, 0},
+        {DETFOLD_PATH_AUTO, 64, 0x7FFFFFFF, 1, DETFOLD_POLICY_CACHED, 0},
+        {7, 0, 0, 0, 0, 0},
+        {DETFOLD_PATH_AUTO, 100, 0, 0, 0, 0},
+        {DETFOLD_PATH_AUTO, 0, -1, 0, 0, 0},
+        {DETFOLD_PATH_AUTO, 0, 0, 3, 0, 0},
+        {DETFOLD_PATH_AUTO, 0, 0, 2, DETFOLD_POLICY_CACHED, 0},
+        {DETFOLD_PATH_AUTO, 0, 0, 0, 9, 0},
     };
     const int nb = (int)(sizeof bases / sizeof bases[0]);
     long calls = 0, accepted = 0;
@@ -112,7 +137,9 @@ int main(void)
                                 ++accepted;
                                 const int co = ((out >> 2) & 3) == ((st >> 2) & 3) && (out & 3) == 0 &&
                                                (st & 3) == 0 && len % 4 == 0;
-                                check_plan(&plan, W, len, co);
+                                const int rows_ovr = ki >= 0 && overrides[ki].path == DETFOLD_PATH_ROWS;
+                                check_plan(&plan, W, len, co, rows_ovr ? overrides[ki].block : 0,
+                                           ki >= 0 ? overrides[ki].group : 0);
                                 sum = sum * 31 + (uint64_t)plan.grid + (uint64_t)plan.path;
                             } else if (rc != DETFOLD_EINVAL && rc != DETFOLD_EOVERLAP) {
                                 fail("unexpected return code", W, len);
@@ -129,8 +156,49 @@ int main(void)
                     ++calls;
                     if (rc == DETFOLD_OK) {
                         ++accepted;
-                        check_plan(&plan, 2, lens[li], 0);
+                        check_plan(&plan, 2, lens[li], 0, 0, 0);
                     }
+                }
+
+    /* batched folds: every job's workgroups, each job at least one, within int32 */
+    static const int64_t jlens[] = {0, 1, 3, 4, 5, 1023, 65537, 10000019, (int64_t)1 << 31,
+                                    (int64_t)1 << 40, INT64_MAX / 64, -1};
+    const int nj = (int)(sizeof jlens / sizeof jlens[0]);
+    detfold_fold_job jobs[DETFOLD_MAX_JOBS + 1];
+    for (int32_t W = -1; W <= 18; ++W)
+        for (int count = 0; count <= DETFOLD_MAX_JOBS + 1; count += (count < 4 ? 1 : 7))
+            for (int rot = 0; rot < nj; ++rot)
+                for (int ph = 0; ph < 4; ++ph) {
+                    uintptr_t out = 0x7F0000000000ull + 4 * (uintptr_t)ph;
+                    uintptr_t arena = (uintptr_t)1 << 56;
+                    int64_t total = 0;
+                    for (int j = 0; j < count; ++j) {
+                        const int64_t n = jlens[(rot + j) % nj];
+                        jobs[j].out = (float *)out;
+                        jobs[j].stacked = (const float *)arena;
+                        jobs[j].len = n;
+                        if (n > 0 && n < ((int64_t)1 << 41)) {
+                            out += (uintptr_t)n * 4 + 4 * (uintptr_t)ph;
+                            arena += (uintptr_t)n * 4 * 20 + 64;
+                        }
+                        total += n > 0 ? n : 0;
+                    }
+                    memset(&plan, 0xA5, sizeof plan);
+                    const int rc = detfold_plan_fold_ranks_batch(jobs, count, W, 256, &plan);
+                    ++calls;
+                    sum = sum * 31 + (uint64_t)rc;
+                    if (rc != DETFOLD_OK)
+                        continue;
+                    ++accepted;
+                    if (plan.group < 1 || plan.group > 64)
+                        fail("batch XCD group out of range", W, count);
+                    if (total == 0 && plan.grid != 0)
+                        fail("empty batch with a grid", W, count);
+                    if (total > 0 && (plan.grid < 1 || plan.grid > 0x7FFFFFFF || plan.tile < 1 ||
+                                      plan.block < 64 || plan.block > 1024))
+                        fail("batch plan out of range", W, count);
+                    if (total > 0 && plan.grid * plan.tile < plan.body)
+                        fail("batch grid does not cover its groups", W, count);
                 }
 
     /* owner shards: coverage, order and balance for every world and length */

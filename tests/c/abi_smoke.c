@@ -13,7 +13,7 @@ int main(void)
     const float *stacked = (const float *)(base + (1u << 30));
     int64_t start[3], length[3];
     detfold_plan plan;
-    detfold_launch launch = {DETFOLD_PATH_ROWS, 0, 0, 0, DETFOLD_POLICY_DEFAULT};
+    detfold_launch launch = {DETFOLD_PATH_ROWS, 0, 0, 0, DETFOLD_POLICY_DEFAULT, 0};
 
     printf("abi %d\n", detfold_abi_version());
     printf("w0 %d\n", fold_ranks(out, stacked, 0, 16, NULL));

@@ -47,12 +47,12 @@ def test_library_exports_nothing_but_the_c_abi(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 9
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 11
 
 
 def test_strerror_covers_every_code(detfold_lib):
     seen = set()
-    for rc in range(0, 6):
+    for rc in range(0, 7):
         s = detfold_lib.strerror(rc)
         assert s and s not in seen
         seen.add(s)
@@ -137,30 +137,56 @@ def test_plan_rows_tile_per_width(detfold_lib, W, kib):
     assert p["grid"] == -(-(n // 4) // p["tile"])
 
 
+def _rule_shape(W, n, coaligned):
+    """The row-body shape and XCD group the plan should pick for a stacked
+    arena of W slots of n floats (slot stride n*4 bytes): slots that do not
+    repeat the address bits below 16 MiB take runs of 8 tiles per XCD from
+    three slots up and two slots per wave from nine up; otherwise eight
+    slots take one slot per wave at lengths that are multiples of 2^24 and
+    two else, five to sixteen take two when co-aligned."""
+    repeat = (n * 4) % (1 << 24) == 0
+    if W < 5 or W > 16:
+        spw = 1
+    elif not repeat:
+        spw = 2 if W >= 9 else 1
+    elif W == 8:
+        spw = 1 if n % (1 << 24) == 0 else 2
+    else:
+        spw = 2 if coaligned else 1
+    group = 8 if (3 <= W <= 16 and not repeat) else 1
+    block = 64 * (-(-W // spw))
+    tile = 64 * (1 if spw == 2 else (8 if W <= 2 else -(-W // 4)))
+    return block, tile, group
+
+
 @pytest.mark.parametrize("n,spw", [(1 << 24, 1), (1 << 25, 1), (3 << 24, 1), (1 << 22, 2), (1 << 23, 2),
-                                   ((1 << 24) + 4, 2), (10_000_000, 2), (12_000_001, 2), (1 << 26, 1)])
+                                   ((1 << 24) + 4, 1), (10_000_000, 1), (12_000_001, 1), (1 << 26, 1),
+                                   (6_291_456, 1)])
 def test_plan_eight_slot_shape_follows_the_slot_length(detfold_lib, n, spw):
-    # W = 8: one slot per wave (8 waves x 2 KiB) when the slot length is a
-    # multiple of 2^24 floats, else two slots per wave (4 waves x 1 KiB each)
+    # W = 8: one slot per wave (8 waves x 2 KiB) at slot lengths that are
+    # multiples of 2^24 floats and at lengths whose slots do not repeat the
+    # low 16 MiB of address (the latter with runs of 8 tiles per XCD); two
+    # slots per wave (4 waves x 1 KiB each) at the other multiples of 2^22
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
     assert (p["block"], p["tile"]) == ((512, 128) if spw == 1 else (256, 64))
+    assert (p["block"], p["tile"], p["group"]) == _rule_shape(8, n, True)
     assert p["grid"] == -(-p["body"] // p["tile"])
-    # an override must name the shape's own workgroup size
-    bad = 256 if spw == 1 else 512
-    with pytest.raises(detfold_lib.DetfoldError):
-        detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU,
-                                    dict(path=detfold_lib.PATH_ROWS, block=bad, grid=0, unroll=0, policy=0))
-    # three and four slots keep one slot per wave at any length; five to
-    # sixteen take two when every slot shares out's phase (an odd width's last
-    # wave streams one; sixteen: see below)
-    for W in (3, 4):
-        q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), W, n, CU)
-        assert q["block"] == 64 * W
-    for W in (5, 6, 7, 10, 12, 13, 14, 15):
-        q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), W, n, CU)
-        two = (64 * (-(-W // 2)), 64)
-        assert (q["block"], q["tile"]) == (two if n % 4 == 0 else (64 * W, 64 * (-(-W // 4))))
+    # an override may name either shape by its workgroup size, and nothing else
+    other = 256 if spw == 1 else 512
+    q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU,
+                                    dict(path=detfold_lib.PATH_ROWS, block=other, grid=0, unroll=0, policy=0))
+    assert (q["block"], q["tile"]) == ((512, 128) if other == 512 else (256, 64))
+    for bad in (128, 384, 448, 1024):
+        with pytest.raises(detfold_lib.DetfoldError):
+            detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU,
+                                        dict(path=detfold_lib.PATH_ROWS, block=bad, grid=0, unroll=0, policy=0))
+    # the other widths, co-aligned and with slot 0 four bytes off out's phase
+    for W in (2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14, 15, 16):
+        for shift in (0, 4):
+            q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34) + shift, W, n, CU)
+            co = shift == 0 and n % 4 == 0
+            assert (q["block"], q["tile"], q["group"]) == _rule_shape(W, n, co), (W, n, shift)
 
 
 @pytest.mark.parametrize("W", [1, 17, 24])
@@ -180,6 +206,7 @@ def test_plan_w4_gradient_arena(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, BASE + 4 * n + 4096, 4, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS and p["body"] == n // 4 and p["tail"] == 0
     assert p["block"] == 256 and p["tile"] == 64 and p["grid"] == -(-(n // 4) // 64)
+    assert p["group"] == 8  # 4e8-byte slots do not repeat the low 16 MiB of address
 
 
 def test_plan_w16_offset_arena(detfold_lib):
@@ -196,7 +223,8 @@ def test_plan_w16_offset_arena(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
     assert (p["head"], p["body"], p["tail"]) == (0, n // 4, 3)
-    assert p["block"] == 1024 and p["tile"] == 256
+    # two slots per wave (8 waves x 1 KiB each), runs of 8 tiles per XCD
+    assert (p["block"], p["tile"], p["group"]) == (512, 64, 8)
     # the direct scalar body stays available
     p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU, dict(path=detfold_lib.PATH_SCALAR,
                                                                    block=0, grid=0, unroll=0, policy=0))
@@ -254,9 +282,10 @@ def test_plan_override(detfold_lib):
     assert (p["path"], p["block"], p["grid"], p["tile"]) == (detfold_lib.PATH_ROWS, 256, 5, 64)
 
 
-@pytest.mark.parametrize("W,launch", [(8, dict(block=512)), (8, dict(unroll=2)),
+@pytest.mark.parametrize("W,launch", [(8, dict(block=384)), (8, dict(unroll=2)), (4, dict(block=128)),
                                       (8, dict(policy=2)), (1, {}), (17, dict(block=256)),
-                                      (24, dict(unroll=2))])
+                                      (24, dict(unroll=2)), (8, dict(group=-1)), (8, dict(group=65)),
+                                      (8, dict(group=3)), (8, dict(group=128))])
 def test_plan_rejects_impossible_row_overrides(detfold_lib, W, launch):
     cfg = dict(path=detfold_lib.PATH_ROWS, block=0, grid=0, unroll=0, policy=0)
     cfg.update(launch)
@@ -473,13 +502,15 @@ def test_plan_wide_rows(detfold_lib, W, n):
 
 @pytest.mark.parametrize("n", [1 << 22, 1 << 24, 3 << 20, 6_000_000, 10_000_000, 10_000_019])
 def test_plan_sixteen_slot_shape_follows_alignment(detfold_lib, n):
-    # W = 16: two slots per wave (8 waves x 1 KiB each) when out and every
-    # slot share one 16-byte phase, one slot per wave (16 waves x 4 KiB) else
-    aligned = n % 4 == 0
+    # W = 16: two slots per wave (8 waves x 1 KiB each) wherever the slots do
+    # not repeat the low 16 MiB of address (with runs of 8 tiles per XCD) or
+    # share out's 16-byte phase; one slot per wave (16 waves x 4 KiB) for
+    # shifted slots at lengths that are multiples of 2^22
+    repeat = (n * 4) % (1 << 24) == 0
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 16, n, CU)
-    assert (p["block"], p["tile"]) == ((512, 64) if aligned else (1024, 256))
+    assert (p["block"], p["tile"], p["group"]) == ((512, 64, 1) if repeat else (512, 64, 8))
     q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, 16, n, CU)  # slot 0 shifted
-    assert (q["block"], q["tile"]) == (1024, 256)
+    assert (q["block"], q["tile"], q["group"]) == ((1024, 256, 1) if repeat else (512, 64, 8))
     for plan in (p, q):
         assert plan["path"] == detfold_lib.PATH_ROWS
         assert plan["grid"] == -(-plan["body"] // plan["tile"])
@@ -577,3 +608,39 @@ def test_batch_plan_covers_every_job(detfold_lib):
         df.plan_fold_ranks_batch([(BASE, scratch, 10)], 1, 256)   # one launch needs 2 <= W <= 16
     with pytest.raises(df.DetfoldError):
         df.plan_fold_ranks_batch([(BASE, scratch, 10)], 17, 256)
+
+
+def test_plan_row_shapes_by_block_and_group(detfold_lib):
+    df = detfold_lib
+    rows = dict(path=df.PATH_ROWS, grid=0, unroll=0, policy=0)
+    for W in range(5, 17):
+        n = 1_000_003
+        one = df.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, W, n, CU, dict(rows, block=64 * W))
+        two = df.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, W, n, CU, dict(rows, block=64 * (-(-W // 2))))
+        assert one["tile"] == 64 * (-(-W // 4)) and two["tile"] == 64
+        assert two["grid"] == -(-two["body"] // 64)
+    for W in (2, 3, 4):
+        with pytest.raises(df.DetfoldError):
+            df.plan_fold_ranks(BASE, BASE + (1 << 34), W, 1000, CU, dict(rows, block=64 * (-(-W // 2))))
+    for W, block, tile in ((17, 1024, 256), (17, 512, 64), (64, 512, 64)):
+        p = df.plan_fold_ranks(BASE, BASE + (1 << 34), W, 1 << 20, CU, dict(rows, block=block))
+        assert (p["block"], p["tile"]) == (block, tile)
+    # the XCD group: the plan's own choice, or the override's
+    p = df.plan_fold_ranks(BASE, BASE + (1 << 34), 16, 10_000_019, CU)
+    assert p["group"] >= 1
+    for g in (1, 2, 8, 64):
+        q = df.plan_fold_ranks(BASE, BASE + (1 << 34), 16, 10_000_019, CU, dict(rows, block=0, group=g))
+        assert q["group"] == g
+    assert df.plan_fold_into(BASE, BASE + (1 << 20), 4096, CU)["group"] == 1
+
+
+def test_pair_link_refuses_stream_capture_before_any_call(detfold_lib, monkeypatch):
+    # the pair link cannot be captured into a graph: with the current stream
+    # capturing, every call raises before it touches a stream or the library
+    import torch
+    link = object.__new__(detfold_lib.PairLink)  # no device needed to reach the check
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(detfold_lib.DetfoldError) as e:
+        link._fork()
+    assert e.value.rc == detfold_lib.ECAPTURE
+    assert "captured" in detfold_lib.strerror(detfold_lib.ECAPTURE)

@@ -271,6 +271,13 @@ GEOMS = [dict(path=p, block=b, grid=g, unroll=u, policy=pol)
 ROW_GEOMS = [dict(path=3, block=b, grid=g, unroll=0, policy=0) for b in (0, -1) for g in (0, 1, 7)]
 
 
+def _row_shape_blocks(W):
+    """Every workgroup size that names a row-body shape at width W."""
+    if W > 16:
+        return [1024, 512]
+    return [64 * W] + ([64 * (-(-W // 2))] if W >= 5 else [])
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 9, 16, 17, 24, 33, 64])
 def test_geometry_independence(env, W):
     df, torch, dev = env
@@ -285,6 +292,9 @@ def test_geometry_independence(env, W):
         cu = torch.cuda.get_device_properties(dev).multi_processor_count
         rb = df.plan_fold_ranks(out.data_ptr(), stacked.data_ptr(), W, n, cu)["block"]
         geoms += [dict(g, block=rb if g["block"] < 0 else 0) for g in ROW_GEOMS]
+        # every shape, with XCD tile groups, in one pass and looping over the tiles
+        geoms += [dict(path=3, block=b, grid=g, unroll=0, policy=0, group=x)
+                  for b in _row_shape_blocks(W) for x in (1, 4, 64) for g in (0, 7)]
     for geom in geoms:
         if W >= 16 and geom["unroll"] == 4 and geom["block"] == 1024:
             continue  # legal but spills registers; covered at smaller blocks

@@ -276,3 +276,58 @@ def test_pair_all_reduce_beside_a_busy_stream(env):
     _assert_bits(xa.cpu().numpy(), oracle.fold_into(ha, hb), "rank 0 beside a busy stream")
     _assert_bits(xb.cpu().numpy(), oracle.fold_into(ha, hb), "rank 1 beside a busy stream")
     busy.synchronize()
+
+
+@pytest.mark.skip(reason="capturing the pair link into a HIP graph ended the test process with a "
+                         "segmentation fault inside hipStreamEndCapture; the cause is not known, so the "
+                         "link now refuses stream capture (DETFOLD_ECAPTURE) and this case stays off")
+@pytest.mark.parametrize("n", [4096, 65536])
+def test_pair_all_reduce_graph_replays(env, n):
+    # One call captured in a HIP graph (both rank streams forked from the
+    # capture stream and joined back), replayed with eager work and host
+    # synchronizations between the replays: replay k must hold 2^(k-1) times
+    # the sum on both ranks, bit for bit.
+    df, torch, dev = env
+    link = df.PairLink(n, device=dev)
+    ha, hb = fold_inputs.vecf(n, 11 + n), fold_inputs.vecf(n, 77 + n)
+    xa = torch.from_numpy(ha).to(dev)
+    xb = torch.from_numpy(hb).to(dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        link.all_reduce(xa, xb)
+    want = oracle.fold_into(ha, hb)
+    for k in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        _assert_bits(xa.cpu().numpy(), want, "rank 0 replay %d" % k)
+        _assert_bits(xb.cpu().numpy(), want, "rank 1 replay %d" % k)
+        want = oracle.fold_into(want, want)
+
+
+def test_pair_all_reduce_orders_against_the_current_stream(env):
+    # The inputs are written on the caller's current stream right before the
+    # call, with no host synchronization: the call must see those writes,
+    # and work queued after it on the current stream must see its result.
+    df, torch, dev = env
+    n = 1 << 18
+    link = df.PairLink(n, device=dev)
+    ha, hb = fold_inputs.vecf(n, 11 + n), fold_inputs.vecf(n, 77 + n)
+    src_a = torch.from_numpy(ha).to(dev)
+    src_b = torch.from_numpy(hb).to(dev)
+    big = torch.from_numpy(fold_inputs.slots("vecf", 8, 1 << 22, 9)).to(dev)
+    big_out = torch.empty(1 << 22, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    xa = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
+    xb = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        df.fold_ranks(big_out, big)  # keep the current stream busy for a while
+    xa.copy_(src_a)
+    xb.copy_(src_b)
+    link.all_reduce(xa, xb)
+    got_a, got_b = xa.clone(), xb.clone()  # queued on the current stream after the call
+    torch.cuda.synchronize()
+    want = oracle.fold_into(ha, hb)
+    _assert_bits(got_a.cpu().numpy(), want, "rank 0 seen from the current stream")
+    _assert_bits(got_b.cpu().numpy(), want, "rank 1 seen from the current stream")
