@@ -432,7 +432,10 @@ def bench_ceiling(args, torch, dev, timer, stacked, out):
 
 def device_info(torch, dev):
     """What the device reports: CU count, peak memory clock and bus width (HIP
-    device attributes), and the HBM rate those imply (two transfers per clock)."""
+    device attributes), and the HBM rate they imply at four transfers per
+    reported memory clock (HBM3E signals 8 Gb/s per pin against the 2 GHz
+    clock this part reports; MI300X's HBM3 has the same ratio, 5.2 Gb/s per
+    pin against 1.3 GHz)."""
     import ctypes
     props = torch.cuda.get_device_properties(dev)
     info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
@@ -445,8 +448,8 @@ def device_info(torch, dev):
             if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev.index or 0) == 0:
                 info[key] = v.value
         if info.get("memory_clock_khz") and info.get("memory_bus_width_bits"):
-            info["hbm_GBps_from_clock_and_width"] = round(
-                2 * info["memory_clock_khz"] * 1e3 * info["memory_bus_width_bits"] / 8 / 1e9, 1)
+            info["hbm_GBps_at_4_transfers_per_clock"] = round(
+                4 * info["memory_clock_khz"] * 1e3 * info["memory_bus_width_bits"] / 8 / 1e9, 1)
     except OSError:
         pass
     return info
@@ -490,6 +493,7 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     same_one = bool(_torch.equal(out_one.view(_torch.int32), out.view(_torch.int32)))
     res["separate_launches"]["bits_equal_whole_fold"] = same_sep
     res["one_launch"]["bits_equal_whole_fold"] = same_one
+    res["one_launch"]["traffic"] = traffic_for("w16_shards_one_launch")
     log("owner shards: %d shard folds of about %d elements: %d launches %.4f ms per set (%.1f GB/s), one "
         "batched launch %.4f ms (%.1f GB/s); bits equal to the whole fold: %s / %s"
         % (W, shards[0][1], W, res["separate_launches"]["ms_per_set"], res["separate_launches"]["GBps"],
@@ -778,6 +782,9 @@ def bench_pair(args, torch, df, dev):
     import fold_inputs
 
     link = df.PairLink(max(JOIN_SIZES), device=dev)
+    # the same link with both ranks on one stream: no hand-off between queues
+    solo = torch.cuda.Stream(device=dev)
+    same = df.PairLink(max(JOIN_SIZES), device=dev, streams=[solo, solo])
     shot = df.OneShotLink(max(JOIN_SIZES), device=dev, stream=torch.cuda.Stream(device=dev))
     cycles_per_ms = sleep_cycles_per_ms(torch)
     rows = []
@@ -803,12 +810,19 @@ def bench_pair(args, torch, df, dev):
             one.append((time.perf_counter() - t1) * 1e6)
         row = {"n": n, "back_to_back_us_per_call": round(b2b, 3),
                "enqueue_to_complete_us_median": round(statistics.median(one), 3),
-               "device_us_per_call": round(pair_device_us(torch, link, xa, xb, cycles_per_ms), 3)}
+               "device_us_per_call": round(pair_device_us(torch, link, xa, xb, cycles_per_ms), 3),
+               "one_stream_device_us_per_call": round(pair_device_us(torch, same, xa, xb, cycles_per_ms), 3),
+               "library_only_device_us_per_call": round(pair_raw_device_us(torch, df, link, xa, xb,
+                                                                           cycles_per_ms), 3),
+               "library_only_one_stream_device_us_per_call": round(
+                   pair_raw_device_us(torch, df, same, xa, xb, cycles_per_ms), 3)}
         row["one_shot"] = bench_one_shot(torch, df, dev, shot, xa, xb)
         rows.append(row)
         log("pair all-reduce n=%6d: %.2f us/call back-to-back, %.2f us call+sync, %.2f us/call on the "
-            "device; one-shot %s" % (n, b2b, statistics.median(one), row["device_us_per_call"],
-                                      row["one_shot"]))
+            "device (%.2f with both ranks on one stream; the library call alone %.2f, one stream %.2f); "
+            "one-shot %s" % (n, b2b, statistics.median(one), row["device_us_per_call"],
+                             row["one_stream_device_us_per_call"], row["library_only_device_us_per_call"],
+                             row["library_only_one_stream_device_us_per_call"], row["one_shot"]))
     words = shot.barrier_words()
     if words != [0, 0]:
         raise RuntimeError("one-shot barrier words %s after the sweep" % words)
@@ -857,26 +871,58 @@ def pair_device_us(torch, link, xa, xb, cycles_per_ms, calls=100, hold_ms=20.0):
     return start.elapsed_time(end) * 1e3 / calls
 
 
+def pair_raw_device_us(torch, df, link, xa, xb, cycles_per_ms, calls=100, hold_ms=20.0):
+    """Device time per call of the library's pair all-reduce itself, without
+    the binding's ordering against the caller's stream: both rank streams are
+    held by a bounded spin kernel while `calls` calls are enqueued through the
+    C ABI; events after the spins and after the last call bracket them (the
+    later end of the two streams counts)."""
+    import ctypes
+    lib = df.load()
+    torch.cuda.synchronize()
+    streams = list(dict.fromkeys(link.streams))  # one or two distinct streams
+    starts, ends = [], []
+    for st in streams:
+        with torch.cuda.stream(st):
+            torch.cuda._sleep(int(hold_ms * cycles_per_ms))
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        starts.append(e)
+    for _ in range(calls):
+        rc = lib.detfold_pair_all_reduce(ctypes.byref(link._c), xa.data_ptr(), xb.data_ptr(), xa.numel())
+        if rc != df.OK:
+            raise df.DetfoldError(rc, "pair_all_reduce")
+    for st in streams:
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        ends.append(e)
+    torch.cuda.synchronize()
+    first = starts[0]
+    return max(first.elapsed_time(e) for e in ends) * 1e3 / calls
+
+
 def bench_one_shot(torch, df, dev, shot, xa, xb):
     """The one-kernel all-reduce on the same buffers: back-to-back through the
-    binding, one call with a host synchronization, and 200 calls captured in
-    one HIP graph (device time per call)."""
+    binding, one call with a host synchronization (both with the link's own
+    stream as the caller's current stream, so no hand-off between queues),
+    and 200 calls captured in one HIP graph (device time per call)."""
     st = shot.stream
-    for _ in range(20):
-        shot.all_reduce(xa, xb)
-    st.synchronize()
-    reps = 500
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        shot.all_reduce(xa, xb)
-    st.synchronize()
-    b2b = (time.perf_counter() - t0) / reps * 1e6
-    one = []
-    for _ in range(200):
-        t1 = time.perf_counter()
-        shot.all_reduce(xa, xb)
+    with torch.cuda.stream(st):
+        for _ in range(20):
+            shot.all_reduce(xa, xb)
         st.synchronize()
-        one.append((time.perf_counter() - t1) * 1e6)
+        reps = 500
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            shot.all_reduce(xa, xb)
+        st.synchronize()
+        b2b = (time.perf_counter() - t0) / reps * 1e6
+        one = []
+        for _ in range(200):
+            t1 = time.perf_counter()
+            shot.all_reduce(xa, xb)
+            st.synchronize()
+            one.append((time.perf_counter() - t1) * 1e6)
     k_graph = 200
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=st):
