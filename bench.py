@@ -459,9 +459,11 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     """The owner-shard form of the offset arena: each of the W owners' shards
     is gathered once (untimed, device copies of the W slices) into a [W][l_p]
     scratch; then per step all W shard folds run into one output at the
-    owners' offsets, once as W separate fold_ranks launches and once as one
-    fold_ranks_batch launch.  Both must equal the whole-arena fold bit for
-    bit.  Same algorithmic bytes as the whole fold."""
+    owners' offsets, as W separate fold_ranks launches and as one
+    fold_ranks_batch launch; and, with no gather, one launch whose jobs read
+    the owners' shards in place from the arena (row stride len).  Each must
+    equal the whole-arena fold bit for bit.  Same algorithmic bytes as the
+    whole fold."""
     import torch as _torch
     shards = df.shard_plan(n, W)
     scratch = [_torch.empty((W, l), dtype=_torch.float32, device=out.device) for _, l in shards]
@@ -477,11 +479,19 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
 
     def one_launch():
         df.fold_ranks_batch(views_one, scratch)
+
+    in_place = [stacked[:, s:s + l] for s, l in shards]  # row stride n: no gather at all
+    out_arena = _torch.empty_like(out)
+    views_arena = [out_arena[s:s + l] for s, l in shards]
+
+    def one_launch_from_arena():
+        df.fold_ranks_batch(views_arena, in_place)
     moved = (W + 1) * n * 4
     res = {"shards": W, "shard_len_max": max(l for _, l in shards),
            "note": "shards gathered once by device copies (untimed); per step every shard fold, "
                    "as separate launches and as one batched launch"}
-    for key, fn in (("separate_launches", separate), ("one_launch", one_launch)):
+    for key, fn in (("separate_launches", separate), ("one_launch", one_launch),
+                    ("one_launch_shards_read_from_the_arena", one_launch_from_arena)):
         settle(timer, fn)
         for _ in range(args.warmup):
             fn()
@@ -491,6 +501,8 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     _torch.cuda.synchronize()
     same_sep = bool(_torch.equal(out_sep.view(_torch.int32), out.view(_torch.int32)))
     same_one = bool(_torch.equal(out_one.view(_torch.int32), out.view(_torch.int32)))
+    same_arena = bool(_torch.equal(out_arena.view(_torch.int32), out.view(_torch.int32)))
+    res["one_launch_shards_read_from_the_arena"]["bits_equal_whole_fold"] = same_arena
     res["separate_launches"]["bits_equal_whole_fold"] = same_sep
     res["one_launch"]["bits_equal_whole_fold"] = same_one
     res["one_launch"]["traffic"] = traffic_for("w16_shards_one_launch")
@@ -498,7 +510,10 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
         "batched launch %.4f ms (%.1f GB/s); bits equal to the whole fold: %s / %s"
         % (W, shards[0][1], W, res["separate_launches"]["ms_per_set"], res["separate_launches"]["GBps"],
            res["one_launch"]["ms_per_set"], res["one_launch"]["GBps"], same_sep, same_one))
-    if not (same_sep and same_one):
+    log("owner shards read in place from the arena (row stride n), one launch: %.4f ms (%.1f GB/s); bits "
+        "equal: %s" % (res["one_launch_shards_read_from_the_arena"]["ms_per_set"],
+                       res["one_launch_shards_read_from_the_arena"]["GBps"], same_arena))
+    if not (same_sep and same_one and same_arena):
         raise RuntimeError("the owner-shard folds differ from the whole-arena fold")
     return res
 

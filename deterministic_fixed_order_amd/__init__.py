@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(PKG, "libdetfold.so")
 OK, EINVAL, EOVERLAP, ELAUNCH, EDEVICE, ESIZE, ECAPTURE = 0, 1, 2, 3, 4, 5, 6
 PATH_AUTO, PATH_VECTOR, PATH_SCALAR, PATH_ROWS = 0, 1, 2, 3
 POLICY_DEFAULT, POLICY_STREAM, POLICY_CACHED = 0, 1, 2
-ABI_VERSION = 11
+ABI_VERSION = 12
 STATIC_STAGE_FLOATS = 1 << 22
 ONE_SHOT_BLOCKS = 64
 ONE_SHOT_FLAG_WORDS = 2 * 2 * ONE_SHOT_BLOCKS
@@ -66,7 +66,8 @@ class Launch(ctypes.Structure):
 
 
 class FoldJob(ctypes.Structure):
-    _fields_ = [("out", ctypes.c_void_p), ("stacked", ctypes.c_void_p), ("len", ctypes.c_int64)]
+    _fields_ = [("out", ctypes.c_void_p), ("stacked", ctypes.c_void_p), ("len", ctypes.c_int64),
+                ("pitch", ctypes.c_int64)]
 
 
 class PairLinkC(ctypes.Structure):
@@ -234,17 +235,41 @@ def _jobs(outs, stackeds):
     W = None
     jobs = (FoldJob * max(len(outs), 1))()
     for j, (out, stacked) in enumerate(zip(outs, stackeds)):
-        w, n = _stacked_shape(out, stacked)
+        w, n, pitch = _pitched_shape(out, stacked)
         if W is not None and w != W:
             raise ValueError("job %d has W=%d, job 0 has W=%d" % (j, w, W))
         W = w
-        jobs[j].out, jobs[j].stacked, jobs[j].len = out.data_ptr(), stacked.data_ptr(), n
+        jobs[j].out, jobs[j].stacked, jobs[j].len, jobs[j].pitch = out.data_ptr(), stacked.data_ptr(), n, pitch
     return jobs, len(outs), (W or 1)
+
+
+def _pitched_shape(out, stacked):
+    """W, len and slot pitch of a [W, len] view whose rows may be padded apart
+    (row stride >= len, elements contiguous within a row)."""
+    import torch
+    _f32_device(out, "out")
+    if not isinstance(stacked, torch.Tensor) or stacked.dtype != torch.float32:
+        raise TypeError("stacked must be a float32 torch.Tensor")
+    if stacked.device.type != "cuda" or stacked.device != out.device:
+        raise ValueError("stacked must be a device tensor on out's device")
+    if stacked.dim() != 2:
+        raise ValueError("stacked must be [W, len], got shape %s" % (tuple(stacked.shape),))
+    W, n = (int(x) for x in stacked.shape)
+    if out.numel() != n:
+        raise ValueError("out has %d elements, stacked rows have %d" % (out.numel(), n))
+    if n > 1 and stacked.stride(1) != 1:
+        raise ValueError("stacked rows must be contiguous")
+    pitch = int(stacked.stride(0)) if W > 1 else n
+    if W > 1 and pitch < n:
+        raise ValueError("stacked rows overlap (row stride %d < len %d)" % (pitch, n))
+    return W, n, pitch
 
 
 def fold_ranks_batch(outs, stackeds, inv_w: Optional[float] = None, stream=None) -> None:
     """``fold_ranks(outs[j], stackeds[j])`` for every j (same W), in one launch
-    where 2 <= W <= 16; with ``inv_w``, ``fold_ranks_scaled`` instead."""
+    where 2 <= W <= 16; with ``inv_w``, ``fold_ranks_scaled`` instead.  Each
+    ``stackeds[j]`` is a [W, len] view whose rows may be padded apart (for
+    instance ``buf.view(W, pitch)[:, :len]``)."""
     jobs, count, W = _jobs(outs, stackeds)
     if count == 0:
         return
@@ -555,10 +580,13 @@ def plan_fold_ranks(out_addr: int, stacked_addr: int, W: int, n: int, cu_count: 
 
 def plan_fold_ranks_batch(jobs: list, W: int, cu_count: int) -> dict:
     """The plan of ``fold_ranks_batch``'s one launch (host only): ``jobs`` is a
-    list of ``(out_addr, stacked_addr, len)``."""
+    list of ``(out_addr, stacked_addr, len)`` or ``(out_addr, stacked_addr,
+    len, pitch)``."""
     arr = (FoldJob * max(len(jobs), 1))()
-    for j, (o, st, n) in enumerate(jobs):
+    for j, job in enumerate(jobs):
+        o, st, n = job[:3]
         arr[j].out, arr[j].stacked, arr[j].len = o, st, n
+        arr[j].pitch = job[3] if len(job) > 3 else 0
     p = Plan()
     _check(load().detfold_plan_fold_ranks_batch(arr, len(jobs), W, cu_count, ctypes.byref(p)),
            "plan_fold_ranks_batch")

@@ -280,14 +280,20 @@ int run_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, bool scale
         any = any || jobs[j].len > 0;
     if (!any)
         return DETFOLD_OK;
-    if (W == 1 || W > kMaxRowsW) {  // no batched body: one launch per job
-        for (int32_t j = 0; j < count && rc == DETFOLD_OK; ++j)
-            rc = run_ranks(jobs[j].out, jobs[j].stacked, W, jobs[j].len, scaled, inv_w, nullptr, stream);
-        return rc;
-    }
     int32_t cu = 0;
     if ((rc = current_cu_count(&cu)) != DETFOLD_OK)
         return rc;
+    if (W == 1 || W > kMaxRowsW) {  // no batched body: one launch per job, at its pitch
+        for (int32_t j = 0; j < count && rc == DETFOLD_OK; ++j) {
+            if (jobs[j].len == 0)
+                continue;
+            const Geometry g = job_geometry(jobs[j], W);
+            detfold_plan p;
+            if ((rc = make_plan(g, cu, nullptr, DETFOLD_POLICY_STREAM, &p)) == DETFOLD_OK)
+                rc = launch_plan(g, p, scaled, inv_w, stream);
+        }
+        return rc;
+    }
     BatchArgs a;
     detfold_plan p;
     if ((rc = plan_batch(jobs, count, W, cu, &a, &p)) != DETFOLD_OK)

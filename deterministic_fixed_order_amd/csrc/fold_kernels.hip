@@ -266,7 +266,7 @@ template <int W, int SPW> struct RowsShape {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Where slot r starts: a table of base pointers passed in the kernel
-// arguments, or, for the batched fold, base + r*len computed in scalar
+// arguments, or, for the batched fold, base + r*pitch computed in scalar
 // registers (a table built in the kernel would live in private memory).
 struct TableSlots {
     const SlotTable &t;
@@ -274,8 +274,8 @@ struct TableSlots {
 };
 struct StrideSlots {
     const float *s0;
-    int64_t len;
-    __device__ const float *operator()(int r) const { return s0 + (int64_t)r * len; }
+    int64_t pitch;
+    __device__ const float *operator()(int r) const { return s0 + (int64_t)r * pitch; }
 };
 
 template <int W, bool SCALED, typename Slots>
@@ -408,15 +408,24 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_batch(Bat
 {
     constexpr int T = RowsShape<W, SPW>::T;
     __shared__ f4 rows[W][T];
-    const int64_t b = xcd_tile(blockIdx.x, gridDim.x, a.group);
+    // the grid is below 2^31 workgroups (the plan sees to it): 32-bit scalar compares
+    const int32_t b = (int32_t)xcd_tile(blockIdx.x, gridDim.x, a.group);
     int j = 0;  // the last job that starts at or before workgroup b
-    for (int k = 1; k < a.count; ++k)
-        if (b >= a.job[k].tile0)
-            j = k;
+    if (a.uniform_tiles > 0) {  // b / T by multiply-high and one correction step
+        uint32_t q = __umulhi((uint32_t)b, a.uniform_magic);
+        if ((uint32_t)b - q * (uint32_t)a.uniform_tiles >= (uint32_t)a.uniform_tiles)
+            ++q;
+        j = (int)q;
+    } else {
+#pragma unroll
+        for (int k = 1; k < kMaxJobs; ++k)
+            if (k < a.count && b >= a.tile0[k])
+                j = k;
+    }
     float *const out = a.job[j].out;
     const int64_t len = a.job[j].len, head = a.job[j].head;
-    const StrideSlots slots{a.job[j].s0, len};
-    const int64_t tile = b - a.job[j].tile0;
+    const StrideSlots slots{a.job[j].s0, a.job[j].pitch};
+    const int64_t tile = (int64_t)(b - a.tile0[j]);
     if (tile == 0)
         rows_edges<W, SCALED>(out, slots, len, head, threadIdx.x, a.inv_w);
     const uint32_t lane = threadIdx.x & 63;

@@ -119,20 +119,30 @@ struct SlotTable {
 };
 
 // Kernel arguments of the batched fold: the jobs with at least one element,
-// in the caller's order; job j owns workgroups [tile0_j, tile0_{j+1}).
+// in the caller's order; job j owns workgroups [tile0[j], tile0[j+1]).  The
+// first workgroups of all jobs sit together at the front, so that a
+// workgroup finds its job from a few wide scalar loads at fixed offsets
+// rather than a chain of dependent ones.
 constexpr int kMaxJobs = DETFOLD_MAX_JOBS;
 struct BatchJob {
     float *out;
-    const float *s0;  // slot 0; slot r at s0 + r*len
+    const float *s0;  // slot 0; slot r at s0 + r*pitch
     int64_t len;
+    int64_t pitch;    // floats between slot starts (>= len)
     int64_t head;     // elements before out's first 16-byte boundary
-    int64_t tile0;    // the job's first workgroup
 };
 struct BatchArgs {
-    BatchJob job[kMaxJobs];
+    int32_t tile0[kMaxJobs];  // each job's first workgroup (the grid is below 2^31)
     int32_t count;
-    int32_t group;  // XCD tile group (xcd_tile) over the launch's workgroups
+    int32_t group;            // XCD tile group (xcd_tile) over the launch's workgroups
     float inv_w;
+    // When every job has the same number of tiles T (balanced owner shards),
+    // uniform_tiles = T and the job of workgroup b is b / T, computed as
+    // q = (b * uniform_magic) >> 32 plus one correction step, with
+    // uniform_magic = floor((2^32 - 1) / T); 0 = look the job up in tile0.
+    int32_t uniform_tiles;
+    uint32_t uniform_magic;
+    BatchJob job[kMaxJobs];
 };
 
 // Kernel arguments of the one-shot all-reduce.
@@ -192,6 +202,9 @@ Geometry into_geometry(uintptr_t dst, uintptr_t stage, int64_t n);
 Geometry slots_geometry(const float *out, const float *const *slots, int32_t W, int64_t len);
 int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length);
 int check_batch_args(const detfold_fold_job *jobs, int32_t count, int32_t W);
+// A batch job's slot pitch (its pitch, or len when 0) and its geometry.
+int64_t job_pitch(const detfold_fold_job &j);
+Geometry job_geometry(const detfold_fold_job &j, int32_t W);
 // The batched fold's kernel arguments and plan (2 <= W <= 16, arguments
 // checked): jobs without elements are dropped; a.count == 0 when none is left.
 int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t cu_count,

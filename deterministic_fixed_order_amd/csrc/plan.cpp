@@ -332,16 +332,45 @@ int balanced_shards(int64_t n, int32_t world, int64_t *start, int64_t *length)
     return DETFOLD_OK;
 }
 
-// Each job as fold_ranks checks it, and no job's output may touch another
-// job's output or arena (the workgroups of one launch run in any order).
+int64_t job_pitch(const detfold_fold_job &j) { return j.pitch ? j.pitch : j.len; }
+
+Geometry job_geometry(const detfold_fold_job &j, int32_t W)
+{
+    const int64_t pitch = job_pitch(j);
+    return Geometry{(uintptr_t)j.out, (uintptr_t)j.stacked, (uintptr_t)j.stacked + (uintptr_t)pitch * 4, pitch, W,
+                    j.len};
+}
+
+// The floats a job's arena spans: (W-1)*pitch + len, or -1 when that
+// overflows the byte range an int64 can hold.
+static int64_t job_span(const detfold_fold_job &j, int32_t W)
+{
+    const int64_t pitch = job_pitch(j);
+    if (pitch > (INT64_MAX / 4 - j.len) / (W > 1 ? W - 1 : 1))
+        return -1;
+    return (int64_t)(W - 1) * pitch + j.len;
+}
+
+// Each job as fold_ranks checks it (its arena spanning (W-1)*pitch + len
+// floats), and no job's output may touch another job's output or arena (the
+// workgroups of one launch run in any order).
 int check_batch_args(const detfold_fold_job *jobs, int32_t count, int32_t W)
 {
     if (count < 0 || count > kMaxJobs || W < 1 || (count > 0 && !jobs))
         return DETFOLD_EINVAL;
     for (int32_t j = 0; j < count; ++j) {
-        const int rc = check_ranks_args(jobs[j].out, jobs[j].stacked, W, jobs[j].len);
-        if (rc != DETFOLD_OK)
-            return rc;
+        const detfold_fold_job &b = jobs[j];
+        if (b.len < 0 || b.pitch < 0 || (b.pitch && b.pitch < b.len))
+            return DETFOLD_EINVAL;
+        if (b.len == 0)
+            continue;
+        if (!b.out || !b.stacked || (((uintptr_t)b.out) & 3) || (((uintptr_t)b.stacked) & 3))
+            return DETFOLD_EINVAL;
+        const int64_t span = job_span(b, W);
+        if (span < 0)
+            return DETFOLD_EINVAL;
+        if (ranges_overlap((uintptr_t)b.out, (uint64_t)b.len * 4, (uintptr_t)b.stacked, (uint64_t)span * 4))
+            return DETFOLD_EOVERLAP;
     }
     for (int32_t j = 0; j < count; ++j) {
         if (jobs[j].len == 0)
@@ -350,9 +379,9 @@ int check_batch_args(const detfold_fold_job *jobs, int32_t count, int32_t W)
         for (int32_t k = 0; k < count; ++k) {
             if (k == j || jobs[k].len == 0)
                 continue;
-            const uint64_t kb = (uint64_t)jobs[k].len * 4;
-            if (ranges_overlap((uintptr_t)jobs[j].out, ob, (uintptr_t)jobs[k].out, kb) ||
-                ranges_overlap((uintptr_t)jobs[j].out, ob, (uintptr_t)jobs[k].stacked, kb * (uint64_t)W))
+            if (ranges_overlap((uintptr_t)jobs[j].out, ob, (uintptr_t)jobs[k].out, (uint64_t)jobs[k].len * 4) ||
+                ranges_overlap((uintptr_t)jobs[j].out, ob, (uintptr_t)jobs[k].stacked,
+                               (uint64_t)job_span(jobs[k], W) * 4))
                 return DETFOLD_EOVERLAP;
         }
     }
@@ -380,8 +409,7 @@ int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t c
     a->group = 1;
     if (longest < 0)
         return DETFOLD_OK;  // nothing to fold
-    const Geometry lg = ranks_geometry((uintptr_t)jobs[longest].out, (uintptr_t)jobs[longest].stacked, W,
-                                       jobs[longest].len);
+    const Geometry lg = job_geometry(jobs[longest], W);
     p->block = rows_block(lg);
     p->tile = rows_tile(lg);
     p->group = rows_group(lg, p->block);
@@ -394,10 +422,11 @@ int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t c
         b.out = jobs[j].out;
         b.s0 = jobs[j].stacked;
         b.len = jobs[j].len;
+        b.pitch = job_pitch(jobs[j]);
         b.head = (4 - phase16((uintptr_t)jobs[j].out)) & 3;
         if (b.head > b.len)
             b.head = b.len;
-        b.tile0 = tiles;
+        a->tile0[a->count - 1] = (int32_t)(tiles < 0x7FFFFFFF ? tiles : 0x7FFFFFFF);
         const int64_t groups = (b.len - b.head) >> 2;
         const int64_t t = (groups + p->tile - 1) / p->tile;
         tiles += t > 0 ? t : 1;
@@ -406,6 +435,13 @@ int plan_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, int32_t c
     if (tiles > 0x7FFFFFFF)
         return DETFOLD_EINVAL;
     p->grid = tiles;
+    // every job the same number of tiles: the kernel divides instead of looking up
+    const int64_t t0 = tiles / a->count;
+    bool uniform = t0 * a->count == tiles;
+    for (int32_t j = 0; uniform && j < a->count; ++j)
+        uniform = a->tile0[j] == (int64_t)j * t0;
+    a->uniform_tiles = uniform ? (int32_t)t0 : 0;
+    a->uniform_magic = uniform ? (uint32_t)(0xFFFFFFFFull / (uint64_t)t0) : 0u;
     return DETFOLD_OK;
 }
 

@@ -140,21 +140,26 @@ int fold_slots_scaled(float *out, const float *const *slots, int32_t W, int64_t 
  * a 40 MB arena is a wave or two of workgroups).  The same holds for any set
  * of buffers of equal width, such as the buckets of one reduction.
  *   jobs     HOST array of `count` jobs (copied into the launch; reusable as
- *            soon as the call returns); a job with len == 0 is skipped
+ *            soon as the call returns); a job with len == 0 is skipped.  A
+ *            job's slots may sit `pitch` floats apart (a receive buffer whose
+ *            slots are padded), which gives the same bits as a packed arena
  *   count    0 <= count <= DETFOLD_MAX_JOBS
  *   W        >= 1, shared by every job.  2 <= W <= 16 is one launch; W = 1
  *            and W > 16 run one launch per job.
- * Every job is checked as fold_ranks checks its arguments; besides, no job's
- * output may overlap another job's output or arena (DETFOLD_EOVERLAP).
- * Arenas may overlap each other (they are only read).
+ * Every job is checked as fold_ranks checks its arguments (its arena being
+ * [stacked, stacked + (W-1)*pitch + len)); besides, no job's output may
+ * overlap another job's output or arena (DETFOLD_EOVERLAP), and a pitch below
+ * len is DETFOLD_EINVAL.  Arenas may overlap each other (they are only read).
  * Errors: DETFOLD_EINVAL (also for count out of range or NULL jobs with
  * count > 0), DETFOLD_EOVERLAP, DETFOLD_EDEVICE, DETFOLD_ELAUNCH.
  */
 #define DETFOLD_MAX_JOBS 32
 typedef struct detfold_fold_job {
     float *out;           /* device, len floats, written */
-    const float *stacked; /* device, [W][len] floats, read */
+    const float *stacked; /* device, slot r at stacked + r*pitch (read) */
     int64_t len;          /* elements per slot, >= 0 */
+    int64_t pitch;        /* floats from one slot's start to the next: 0 = len (a packed
+                             [W][len] arena), else >= len (slots padded apart) */
 } detfold_fold_job;
 int fold_ranks_batch(const detfold_fold_job *jobs, int32_t count, int32_t W, void *stream);
 
@@ -363,7 +368,7 @@ int detfold_one_shot_rank(const detfold_one_shot_link *link, int32_t rank, float
 const char *detfold_strerror(int rc);
 
 /* ABI revision of this header; bumped on any incompatible change. */
-#define DETFOLD_ABI_VERSION 11
+#define DETFOLD_ABI_VERSION 12
 int detfold_abi_version(void);
 
 /* ------------------------------------------------------------------------

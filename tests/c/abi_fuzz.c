@@ -177,9 +177,13 @@ int main(void)
                         jobs[j].out = (float *)out;
                         jobs[j].stacked = (const float *)arena;
                         jobs[j].len = n;
+                        /* packed, padded, below len (rejected) and past any range (rejected) */
+                        const int pk = (rot + j + ph) % 4;
+                        jobs[j].pitch = pk == 0 ? 0 : pk == 1 ? (n > 0 ? n + 7 : 0)
+                                        : pk == 2 ? (n > 1 ? n - 1 : 0) : INT64_MAX / 2;
                         if (n > 0 && n < ((int64_t)1 << 41)) {
                             out += (uintptr_t)n * 4 + 4 * (uintptr_t)ph;
-                            arena += (uintptr_t)n * 4 * 20 + 64;
+                            arena += ((uintptr_t)n + 8) * 4 * 20 + 64;
                         }
                         total += n > 0 ? n : 0;
                     }

@@ -47,7 +47,7 @@ def test_library_exports_nothing_but_the_c_abi(detfold_lib):
 
 
 def test_abi_version(detfold_lib):
-    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 11
+    assert detfold_lib.load().detfold_abi_version() == detfold_lib.ABI_VERSION == 12
 
 
 def test_strerror_covers_every_code(detfold_lib):
@@ -574,6 +574,26 @@ def test_batch_rejects_bad_arguments(detfold_lib):
     p = df.plan_fold_ranks_batch([(o[0], st[0], 1000), (o[0] + 4000, st[0], 1000)], 4, 256)
     assert p["grid"] >= 2
     assert lib.fold_ranks_batch_scaled(good, 2, 0, ctypes.c_float(0.5), None) == EINVAL
+    # a slot pitch: 0 (packed) or at least len; the arena spans (W-1)*pitch + len
+    j = _jobs(df, (o[0], st[0], 1000))
+    j[0].pitch = 999
+    assert lib.fold_ranks_batch(j, 1, 4, None) == EINVAL
+    j[0].pitch = -1
+    assert lib.fold_ranks_batch(j, 1, 4, None) == EINVAL
+    j[0].pitch = 2 ** 61
+    assert lib.fold_ranks_batch(j, 1, 4, None) == EINVAL                          # span overflows
+    j = _jobs(df, (st[0] + 3 * 4096 * 4 + 64, st[0], 1000))                       # inside slot 3 at pitch 4096
+    j[0].pitch = 4096
+    assert lib.fold_ranks_batch(j, 1, 4, None) == EOVERLAP
+    j[0].pitch = 0                                                                # packed: past the arena
+    assert df.plan_fold_ranks_batch([(st[0] + 3 * 4096 * 4 + 64, st[0], 1000)], 4, 256)["grid"] >= 1
+    # a padded arena spans 3*5000 + 1000 floats, its padding included: another
+    # job's output may start right after it, not inside it
+    assert df.plan_fold_ranks_batch([(o[0], st[0], 1000, 5000), (st[0] + 4 * 16_000, st[1], 1000)], 4,
+                                    256)["grid"] >= 2
+    for inside in (5_500, 12_000, 15_999):
+        with pytest.raises(df.DetfoldError):
+            df.plan_fold_ranks_batch([(o[0], st[0], 1000, 5000), (st[0] + 4 * inside, st[1], 1000)], 4, 256)
 
 
 def test_batch_plan_covers_every_job(detfold_lib):
@@ -644,3 +664,15 @@ def test_pair_link_refuses_stream_capture_before_any_call(detfold_lib, monkeypat
         link._fork()
     assert e.value.rc == detfold_lib.ECAPTURE
     assert "captured" in detfold_lib.strerror(detfold_lib.ECAPTURE)
+
+
+def test_batch_plan_follows_the_pitch(detfold_lib):
+    # the shape rule reads the slot pitch: 625,002-float slots packed repeat no
+    # low 16 MiB of address (two slots per wave, runs of 8 tiles per XCD);
+    # padded to 2^22 floats (16 MiB) apart they do
+    df = detfold_lib
+    packed = df.plan_fold_ranks_batch([(BASE, BASE + (1 << 34), 625_002)], 16, 256)
+    padded = df.plan_fold_ranks_batch([(BASE, BASE + (1 << 34), 625_002, 1 << 22)], 16, 256)
+    assert (packed["block"], packed["tile"], packed["group"]) == (512, 64, 8)
+    assert (padded["block"], padded["tile"], padded["group"]) == (512, 64, 1)
+    assert packed["body"] == padded["body"] and packed["grid"] == padded["grid"]

@@ -132,3 +132,55 @@ def test_adjacent_outputs_in_one_buffer_and_shared_arena(detfold_lib):
     for r in range(len(cuts) - 1):
         assert np.array_equal(_bits(out[r].cpu().numpy()), _bits(want)), r
     assert np.array_equal(_bits(flat.cpu().numpy()), _bits(want))
+
+
+@pytest.mark.parametrize("W,pad", [(2, 3), (5, 1024), (8, 1 << 20), (16, 7), (16, (1 << 22) - 625_002)])
+def test_padded_slots_give_the_bits_of_a_packed_arena(detfold_lib, W, pad):
+    # each job's slots sit len + pad floats apart (a receive buffer with
+    # padded slots): the bits must be those of the packed fold
+    import torch
+    df = detfold_lib
+    dev = torch.device("cuda:0")
+    lens = [625_002, 1, 4099, 0, 77_777] if W == 16 else [1000, 3, 65_539, 12_345]
+    print("case: padded batch W=%d pad=%d" % (W, pad), flush=True)
+    outs, views, hosts, bufs = [], [], [], []
+    for j, ln in enumerate(lens):
+        pitch = ln + pad
+        host = fold_inputs.slots("varied", W, ln, 6500 + j + W, spread=3.0)
+        off = j % 4
+        buf = torch.full((W * pitch + off,), float("nan"), dtype=torch.float32, device=dev)
+        view = buf[off:off + W * pitch].view(W, pitch)[:, :ln]
+        view.copy_(torch.from_numpy(host))
+        o = torch.full((ln,), float("nan"), dtype=torch.float32, device=dev)
+        outs.append(o)
+        views.append(view)
+        hosts.append(host)
+        bufs.append(buf)
+    for inv_w in (None, 1.0 / W):
+        df.fold_ranks_batch(outs, views, inv_w=inv_w)
+        torch.cuda.synchronize()
+        for j, (o, host) in enumerate(zip(outs, hosts)):
+            want = oracle.fold_stacked(host) if inv_w is None else oracle.fold_stacked_scaled(host, np.float32(inv_w))
+            assert np.array_equal(_bits(o.cpu().numpy()), _bits(want)), "job %d len %d" % (j, lens[j])
+
+
+@pytest.mark.parametrize("W", [1, 17])
+def test_padded_slots_with_one_launch_per_job(detfold_lib, W):
+    import torch
+    df = detfold_lib
+    dev = torch.device("cuda:0")
+    print("case: padded batch W=%d (one launch per job)" % W, flush=True)
+    lens, pad = [5, 70_001, 4096], 13
+    outs, views, hosts = [], [], []
+    for j, ln in enumerate(lens):
+        host = fold_inputs.slots("varied", W, ln, 6600 + j, spread=2.0)
+        buf = torch.empty(W * (ln + pad) + 1, dtype=torch.float32, device=dev)
+        view = buf[1:1 + W * (ln + pad)].view(W, ln + pad)[:, :ln]
+        view.copy_(torch.from_numpy(host))
+        outs.append(torch.empty(ln, dtype=torch.float32, device=dev))
+        views.append(view)
+        hosts.append(host)
+    df.fold_ranks_batch(outs, views)
+    torch.cuda.synchronize()
+    for o, host in zip(outs, hosts):
+        assert np.array_equal(_bits(o.cpu().numpy()), _bits(oracle.fold_stacked(host)))
