@@ -237,13 +237,14 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
     fold_tiles<WS, U, float, SCALED, POL>(out, s0, s1, stride, w, len, inv_w);
 }
 
-// LDS row-transpose body (2 <= W <= 16).  One workgroup of ceil(W/SPW) waves
-// folds a tile of T 16-byte groups of `out`: wave q streams the tile's bytes
-// of its slots q*SPW .. q*SPW+SPW-1 that exist -- LPW consecutive KiB of each,
-// one contiguous run per slot -- straight into LDS rows (buffer loads with the
-// lds bit, no register staging); after a barrier every thread folds whole
-// groups from the W rows, in ascending row order, and stores them.  SPW is 1
-// or 2 (two slots of 1 KiB per wave; the plan's rows_slots_per_wave picks).
+// LDS row-transpose body (2 <= W <= 16).  One workgroup of rows_waves(W, SPW)
+// waves folds a tile of T 16-byte groups of `out`: wave q streams the tile's
+// bytes of its slots (a run of at most SPW consecutive slots, rows_wave_lo)
+// -- LPW consecutive KiB of each, one contiguous run per slot -- straight into
+// LDS rows (buffer loads with the lds bit, no register staging); after a
+// barrier every thread folds whole groups from the W rows, in ascending row
+// order, and stores them.  SPW is 1 or 2 (up to two slots of 1 KiB per wave;
+// the plan's rows_slots_per_wave picks).
 // Streaming whole runs of a slot keeps each wave on few runs of HBM rows; the
 // direct body instead has every wave touch W runs 1 KiB at a time, which
 // measured 3-8% slower on MI355X.
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_fold_scalar(float *out, const flo
 template <int W, int SPW> struct RowsShape {
     static constexpr int LPW = rows_kib_per_wave(W, SPW);  // KiB of each slot a wave streams per tile
     static constexpr int T = LPW * 64;                     // 16-byte groups per tile
-    static constexpr int WAVES = rows_waves(W, SPW);       // wave q streams slots q*SPW .. q*SPW+SPW-1 < W
+    static constexpr int WAVES = rows_waves(W, SPW);       // wave q streams its run of slots (rows_wave_lo)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -290,18 +291,20 @@ __device__ __forceinline__ void fold_one_table(float *out, const Slots &slot, in
     out[i] = acc;
 }
 
-// Wave `wave` streams the tile's bytes of its slots (wave*SPW .. wave*SPW+SPW-1
-// that exist) into their LDS rows: LPW KiB of each, through a descriptor based
-// at the slot's element e0 and limited to the tile's cnt groups.
+// Wave `wave` streams the tile's bytes of its slots (its run of at most SPW,
+// rows_wave_lo) into their LDS rows: LPW KiB of each, through a descriptor
+// based at the slot's element e0 and limited to the tile's cnt groups.
 template <int W, int SPW, int LPW, int T, typename Slots>
 __device__ __forceinline__ void stream_rows(f4 (&rows)[W][T], const Slots &slot, int64_t e0,
                                             int64_t cnt, uint32_t wave, uint32_t lane)
 {
+    const uint32_t lo = (uint32_t)rows_wave_lo(W, SPW, (int)wave);
+    const uint32_t hi = (uint32_t)rows_wave_lo(W, SPW, (int)wave + 1);
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-        const uint32_t r = wave * SPW + j;
-        if (r >= (uint32_t)W)
-            break;  // an odd width's last wave streams one slot
+        const uint32_t r = lo + (uint32_t)j;
+        if (r >= hi)
+            break;  // this wave has fewer slots
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot(r) + e0, (uint32_t)(cnt * 16));
 #pragma unroll
         for (int u = 0; u < LPW; ++u)
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_batch(Bat
 // buffers): every slot ends holding the fold of all.  The loads are the row
 // body's; then each thread that owns a group folds it in ascending row order
 // and leaves the sum in row 0, and after a second barrier wave q writes the
-// tile of row 0 into its own slots q*SPW .. q*SPW+SPW-1, through a descriptor
+// tile of row 0 into the slots it loaded (rows_wave_lo), through a descriptor
 // based at each slot's first element of the tile as its loads were, so any
 // 16-byte phase works.  A workgroup has read its tile of every slot (first
 // barrier) before it writes any of them, and workgroups own disjoint tiles;
@@ -483,11 +486,13 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
         }
         __syncthreads();  // the sums are in row 0
 
+        const uint32_t lo = (uint32_t)rows_wave_lo(W, SPW, (int)wave);
+        const uint32_t hi = (uint32_t)rows_wave_lo(W, SPW, (int)wave + 1);
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
-            const uint32_t r = wave * SPW + j;
-            if (r >= (uint32_t)W)
-                break;  // an odd width's last wave streams one slot
+            const uint32_t r = lo + (uint32_t)j;
+            if (r >= hi)
+                break;  // this wave has fewer slots
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {

@@ -39,8 +39,10 @@ constexpr int rows_kib_per_wave(int w)
 }
 
 // Widths from five to sixteen have a second shape, in which each wave streams
-// 1 KiB of two slots per tile (SPW = 2; an odd width's last wave streams one;
-// the plan picks it, see rows_slots_per_wave).  Measured on MI355X:
+// 1 KiB of up to two slots per tile (SPW = 2; rows_waves and rows_wave_lo
+// below say which; the plan picks the shape, see rows_slots_per_wave).  The
+// first measurements on MI355X, before XCD tile groups (the notes on
+// kRepeatBytes say what changed with them):
 //  * W = 8, two slots per wave (four waves): 1.5-12% faster wherever the slot
 //    length is not a multiple of 2^24 floats, 0.8-1.4% slower where it is
 //    (2^24, 2^25, 2^26), whose 64 MiB-aligned runs the one-slot shape suits;
@@ -48,13 +50,13 @@ constexpr int rows_kib_per_wave(int w)
 //    16-byte phase, 0.4-4.3% faster than four slots per wave (four waves) on
 //    the stacked fold at six lengths, 1.4-6% on separate slots, 2-16% on the
 //    fused round, and up to 30% faster than one slot per wave (16 waves x
-//    4 KiB); with shifted slots one slot per wave stays best (several slots
-//    per wave lose 3-12%);
+//    4 KiB); with shifted slots and plain round-robin tiles one slot per
+//    wave was best (several slots per wave lost 3-12%);
 //  * W = 6, 10, 12, 14, every slot at out's phase: 3.7-15% faster than one
 //    slot per wave at slot lengths of 6e6 to 1.26e7 (arenas beyond the
-//    memory-side cache); with shifted slots it loses up to 5% at W = 10 and
-//    12, so shifted arenas keep one slot per wave.  W = 4 keeps one slot per
-//    wave: two lose 6-8% at 2^24 and 1e8;
+//    memory-side cache); with shifted slots and plain round-robin tiles it
+//    lost up to 5% at W = 10 and 12.  W = 4 keeps one slot per wave: two
+//    lose 6-8% at 2^24 and 1e8;
 //  * odd W = 5, 7, 9, 11 at out's phase: 4-21% faster; 13 and 15: 0.2-5.6%;
 //    W = 3 loses up to 3% and keeps one slot per wave.
 // The shapes differ only in which wave loads which slot; every element's
@@ -73,16 +75,48 @@ constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot len
 // length is such a multiple (W=8 x 2^24, W=4 x 2^24, W=2 x 2^26) plain
 // round-robin stays best: groups lose up to 8% (W=8), and groups of 2 or 4
 // up to 35% at W=4.  At W=2 groups of 8 lose up to 2.5%, so two-slot folds
-// keep plain round-robin.
+// keep plain round-robin.  Later sweeps (6 interleaved rounds each, every
+// variant bit-checked) refined this:
+//  * Co-aligned arenas of five to ten slots whose slots do not repeat take
+//    runs of kSlotGroupMid tiles: +0.3% to +3.2% against runs of 8 over 11
+//    arenas (W=8 x 3*10^7: 6,536 -> 6,745 GB/s), never a loss; from eleven
+//    slots up runs of 32 tie or lose up to 1.9%.
+//  * Shifted arenas (some slot off out's 16-byte phase) whose slot length is
+//    a multiple of kRepeatBytes were a cliff under one slot per wave and
+//    plain round-robin: 4.9-5.6 TB/s at slot lengths 2^22 to 3*2^22 for
+//    W = 5..16.  Runs of 32 tiles per XCD, with two slots per wave from
+//    seven slots up (eight slots excepted), measured +10% to +36% there
+//    (W=16 x 2^22 at base+1: 4,950 -> 6,747 GB/s; W=9 x 3*2^22: +28%), +5%
+//    at W=8 x 2^24 at base+1 and a tie at W=16 x 2^24.  Shifted arenas whose
+//    slots do not repeat tie or gain up to 2.2% with runs of 32 against 8
+//    (the W=16 x 10,000,019 arena at base+1: +0.1% to +0.4%); three slots
+//    keep runs of 8 (runs of 32 lose up to 1.2%).
+//  * Seven slots take two slots per wave on every stacked arena: one slot
+//    per wave means seven-wave workgroups, 28 of a CU's 32 wave slots
+//    (+3% to +6% at slot lengths 10^7 and 1.5*10^7).
 constexpr int64_t kRepeatBytes = (int64_t)1 << 24;
 constexpr int kSlotGroup = 8;
+constexpr int kSlotGroupMid = 32;
 constexpr int rows_kib_per_wave(int w, int spw)
 {
     return spw == 1 ? rows_kib_per_wave(w) : 1;
 }
 
-// Waves of the row body: wave q streams slots q*spw .. q*spw+spw-1 that exist.
-constexpr int rows_waves(int w, int spw) { return (w + spw - 1) / spw; }
+// Waves of the row body: w with one slot per wave; with two, ceil(w/2),
+// except eight at thirteen and fourteen slots.  A CU holds 32 waves, so
+// workgroups of seven waves fill only 28 of them (four workgroups); eight-wave
+// workgroups fill all 32.  Measured on MI355X (6 interleaved rounds,
+// bit-checked), eight waves against seven: +11% to +15% at W = 13 and 14,
+// co-aligned and shifted (W=14 x 8e6: 5,961 -> 6,741 GB/s).
+constexpr int rows_waves(int w, int spw)
+{
+    return spw == 2 && (w == 13 || w == 14) ? 8 : (w + spw - 1) / spw;
+}
+
+// Slots [rows_wave_lo(w, spw, q), rows_wave_lo(w, spw, q + 1)) are wave q's:
+// the w slots in ascending runs over the waves, at most spw per wave (one or
+// two each where there are more waves than ceil(w/spw)).
+constexpr int rows_wave_lo(int w, int spw, int q) { return q * w / rows_waves(w, spw); }
 
 // The slots per wave of a row-body workgroup of `waves` waves over w slots
 // (the inverse of rows_waves for the shapes the plan makes).

@@ -38,21 +38,25 @@ bool slots_repeat(const Geometry &g)
 }
 
 // Slots each wave of the row body streams.
-//  * Stacked arenas whose slots do not repeat the low address bits: two from
-//    nine slots up, else one (with the XCD tile group of rows_group).
-//  * Otherwise: for eight slots two, unless the slot length is a multiple of
-//    kOneSlotAlign; for the other widths from five to sixteen two when every
-//    slot shares out's 16-byte phase (an odd width's last wave streams one);
-//    one otherwise.
+//  * Separate slot buffers (a table): two for eight slots and for five to
+//    sixteen slots that all share out's 16-byte phase, else one.
+//  * Stacked arenas of eight slots: one where the slot length is a multiple
+//    of kOneSlotAlign or the slots do not repeat the low address bits, else
+//    two.
+//  * Stacked arenas of seven and of nine to sixteen slots: two.
+//  * Stacked arenas of five or six slots: two when every slot shares out's
+//    phase and the slots repeat the low address bits, else one.
 int rows_slots_per_wave(const Geometry &g)
 {
     if (g.w > kMaxRowsW || g.w < 5)
         return 1;
-    if (!slots_repeat(g))
-        return g.w >= 9 ? 2 : 1;
+    if (g.has_table)
+        return g.w == 8 || vector_legal(g) ? 2 : 1;
     if (g.w == 8)
-        return !g.has_table && g.stride % kOneSlotAlign == 0 ? 1 : 2;
-    return vector_legal(g) ? 2 : 1;
+        return g.stride % kOneSlotAlign == 0 || !slots_repeat(g) ? 1 : 2;
+    if (g.w == 7 || g.w >= 9)
+        return 2;
+    return vector_legal(g) && slots_repeat(g) ? 2 : 1;
 }
 
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per
@@ -93,15 +97,22 @@ int64_t rows_tile_for_block(const Geometry &g, int block)
     return 0;
 }
 
-// XCD tile group of the row body (xcd_tile in fold_kernels.hip): runs of
-// kSlotGroup tiles per XCD for a stacked arena of three to sixteen slots that
-// do not repeat the low address bits, plain round-robin otherwise.
+// XCD tile group of the row body (xcd_tile in fold_kernels.hip), for stacked
+// arenas of three to sixteen slots: with slots shifted from out's 16-byte
+// phase, runs of kSlotGroupMid tiles per XCD (kSlotGroup at three slots);
+// co-aligned, plain round-robin where the slots repeat the low address bits,
+// else runs of kSlotGroupMid tiles from five to ten slots and of kSlotGroup
+// otherwise.  Separate slot buffers keep plain round-robin.
 int rows_group(const Geometry &g, int block)
 {
     (void)block;
-    if (g.w < 3 || g.w > kMaxRowsW || slots_repeat(g))
+    if (g.w < 3 || g.w > kMaxRowsW || g.has_table)
         return 1;
-    return kSlotGroup;
+    if (!vector_legal(g))
+        return g.w == 3 ? kSlotGroup : kSlotGroupMid;
+    if (slots_repeat(g))
+        return 1;
+    return g.w >= 5 && g.w <= 10 ? kSlotGroupMid : kSlotGroup;
 }
 
 // Positions per thread per pass.  The vector body moves 16 bytes per slot per

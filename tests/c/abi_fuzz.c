@@ -57,17 +57,24 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
             fail("row body override not kept", W, len);
         return;
     }
-    /* slots that do not repeat the low 16 MiB of address: two slots per wave
-     * from nine up and runs of 8 tiles per XCD from three up */
+    /* slots per wave: eight slots one where len is a multiple of 2^24 or the
+     * slots do not repeat the low 16 MiB of address, else two; seven and nine
+     * to sixteen two; five and six two only co-aligned and repeating.  XCD
+     * group: shifted slots runs of 32 (8 at three slots); co-aligned plain
+     * round-robin when repeating, else 32 from five to ten slots and 8 */
     const int repeat = len % ((int64_t)1 << 22) == 0;
     const int spw = (W < 5 || W > 16) ? 1
-                    : !repeat ? (W >= 9 ? 2 : 1)
-                    : W == 8 ? (len % ((int64_t)1 << 24) != 0 ? 2 : 1)
-                    : coaligned ? 2 : 1;
-    if (p->path == DETFOLD_PATH_ROWS && W <= 16 &&
-        p->group != (forced_group ? forced_group : (W >= 3 && !repeat) ? 8 : 1))
+                    : W == 8 ? ((len % ((int64_t)1 << 24) == 0 || !repeat) ? 1 : 2)
+                    : (W == 7 || W >= 9) ? 2
+                    : (coaligned && repeat) ? 2 : 1;
+    const int group = (W < 3 || W > 16) ? 1
+                      : !coaligned ? (W == 3 ? 8 : 32)
+                      : repeat ? 1 : (W >= 5 && W <= 10 ? 32 : 8);
+    if (p->path == DETFOLD_PATH_ROWS && W <= 16 && p->group != (forced_group ? forced_group : group))
         fail("row body with the wrong XCD group", W, len);
-    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * ((W + spw - 1) / spw) : coaligned ? 512 : 1024))
+    /* two slots per wave: ceil(W/2) waves, eight at thirteen and fourteen slots */
+    const int waves = W > 16 ? 0 : (spw == 2 && (W == 13 || W == 14)) ? 8 : (W + spw - 1) / spw;
+    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * waves : coaligned ? 512 : 1024))
         fail("row body with the wrong workgroup size", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W <= 16 && spw == 2 && p->tile != 64)
         fail("two-slot row body with the wrong tile", W, len);

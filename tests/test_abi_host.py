@@ -125,36 +125,57 @@ def test_plan_w8_64mib_per_slot(detfold_lib):
     assert p["policy"] == detfold_lib.POLICY_STREAM
 
 
-@pytest.mark.parametrize("W,kib", [(2, 8), (3, 1), (4, 1), (5, 2), (7, 2), (8, 2), (9, 3),
-                                   (12, 3), (13, 4), (16, 4)])
-def test_plan_rows_tile_per_width(detfold_lib, W, kib):
+@pytest.mark.parametrize("W", [2, 3, 4, 5, 6, 7, 8, 9, 12, 13, 14, 16])
+def test_plan_rows_tile_per_width(detfold_lib, W):
     # a slot length that is a multiple of 2^24 and slots shifted 4 bytes from
-    # out's 16-byte phase: one slot per wave at every width
+    # out's 16-byte phase: one slot per wave of ceil(W/4) KiB (8 KiB at two
+    # slots) up to six slots and at eight, two slots per wave of 1 KiB at
+    # seven and from nine up (eight waves at 13 and 14)
     n = 1 << 24
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 32) + 4, W, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
-    assert p["block"] == 64 * W and p["tile"] == 64 * kib  # kib KiB of each slot per wave
+    assert (p["block"], p["tile"], p["group"]) == _rule_shape(W, n, False)
+    if W <= 6 or W == 8:
+        assert p["block"] == 64 * W and p["tile"] == 64 * (8 if W == 2 else -(-W // 4))
+    else:
+        assert p["block"] == 64 * (8 if W in (13, 14) else -(-W // 2)) and p["tile"] == 64
     assert p["grid"] == -(-(n // 4) // p["tile"])
+
+
+def _rows_waves(W, spw):
+    """Waves of a row-body workgroup: W with one slot per wave; with two,
+    ceil(W/2), but eight at 13 and 14 slots (workgroups of seven waves fill
+    only 28 of a CU's 32 wave slots)."""
+    return 8 if spw == 2 and W in (13, 14) else -(-W // spw)
 
 
 def _rule_shape(W, n, coaligned):
     """The row-body shape and XCD group the plan should pick for a stacked
-    arena of W slots of n floats (slot stride n*4 bytes): slots that do not
-    repeat the address bits below 16 MiB take runs of 8 tiles per XCD from
-    three slots up and two slots per wave from nine up; otherwise eight
-    slots take one slot per wave at lengths that are multiples of 2^24 and
-    two else, five to sixteen take two when co-aligned."""
+    arena of W slots of n floats (slot stride n*4 bytes).  Slots per wave:
+    eight slots take one where n is a multiple of 2^24 or the slots do not
+    repeat the address bits below 16 MiB, else two; seven and nine to sixteen
+    take two; five and six take two only when co-aligned and repeating.  XCD
+    group: shifted slots take runs of 32 tiles (8 at three slots); co-aligned
+    ones plain round-robin when repeating, else runs of 32 from five to ten
+    slots and of 8 otherwise."""
     repeat = (n * 4) % (1 << 24) == 0
     if W < 5 or W > 16:
         spw = 1
-    elif not repeat:
-        spw = 2 if W >= 9 else 1
     elif W == 8:
-        spw = 1 if n % (1 << 24) == 0 else 2
+        spw = 1 if (n % (1 << 24) == 0 or not repeat) else 2
+    elif W == 7 or W >= 9:
+        spw = 2
     else:
-        spw = 2 if coaligned else 1
-    group = 8 if (3 <= W <= 16 and not repeat) else 1
-    block = 64 * (-(-W // spw))
+        spw = 2 if (coaligned and repeat) else 1
+    if W < 3 or W > 16:
+        group = 1
+    elif not coaligned:
+        group = 8 if W == 3 else 32
+    elif repeat:
+        group = 1
+    else:
+        group = 32 if 5 <= W <= 10 else 8
+    block = 64 * _rows_waves(W, spw)
     tile = 64 * (1 if spw == 2 else (8 if W <= 2 else -(-W // 4)))
     return block, tile, group
 
@@ -165,7 +186,7 @@ def _rule_shape(W, n, coaligned):
 def test_plan_eight_slot_shape_follows_the_slot_length(detfold_lib, n, spw):
     # W = 8: one slot per wave (8 waves x 2 KiB) at slot lengths that are
     # multiples of 2^24 floats and at lengths whose slots do not repeat the
-    # low 16 MiB of address (the latter with runs of 8 tiles per XCD); two
+    # low 16 MiB of address (the latter with runs of 32 tiles per XCD); two
     # slots per wave (4 waves x 1 KiB each) at the other multiples of 2^22
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 8, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
@@ -223,8 +244,8 @@ def test_plan_w16_offset_arena(detfold_lib):
     p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU)
     assert p["path"] == detfold_lib.PATH_ROWS
     assert (p["head"], p["body"], p["tail"]) == (0, n // 4, 3)
-    # two slots per wave (8 waves x 1 KiB each), runs of 8 tiles per XCD
-    assert (p["block"], p["tile"], p["group"]) == (512, 64, 8)
+    # two slots per wave (8 waves x 1 KiB each), runs of 32 tiles per XCD
+    assert (p["block"], p["tile"], p["group"]) == (512, 64, 32)
     # the direct scalar body stays available
     p = detfold_lib.plan_fold_ranks(BASE, stacked, 16, n, CU, dict(path=detfold_lib.PATH_SCALAR,
                                                                    block=0, grid=0, unroll=0, policy=0))
@@ -502,15 +523,18 @@ def test_plan_wide_rows(detfold_lib, W, n):
 
 @pytest.mark.parametrize("n", [1 << 22, 1 << 24, 3 << 20, 6_000_000, 10_000_000, 10_000_019])
 def test_plan_sixteen_slot_shape_follows_alignment(detfold_lib, n):
-    # W = 16: two slots per wave (8 waves x 1 KiB each) wherever the slots do
-    # not repeat the low 16 MiB of address (with runs of 8 tiles per XCD) or
-    # share out's 16-byte phase; one slot per wave (16 waves x 4 KiB) for
-    # shifted slots at lengths that are multiples of 2^22
+    # W = 16: two slots per wave (8 waves x 1 KiB each) on every stacked
+    # arena; co-aligned slots take runs of 8 tiles per XCD where they do not
+    # repeat the low 16 MiB of address (plain round-robin where they do),
+    # shifted slots runs of 32
     repeat = (n * 4) % (1 << 24) == 0
     p = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34), 16, n, CU)
-    assert (p["block"], p["tile"], p["group"]) == ((512, 64, 1) if repeat else (512, 64, 8))
+    if n % 4:  # slot r at phase r*n mod 4: shifted slots
+        assert (p["block"], p["tile"], p["group"]) == (512, 64, 32)
+    else:
+        assert (p["block"], p["tile"], p["group"]) == ((512, 64, 1) if repeat else (512, 64, 8))
     q = detfold_lib.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, 16, n, CU)  # slot 0 shifted
-    assert (q["block"], q["tile"], q["group"]) == ((1024, 256, 1) if repeat else (512, 64, 8))
+    assert (q["block"], q["tile"], q["group"]) == (512, 64, 32)
     for plan in (p, q):
         assert plan["path"] == detfold_lib.PATH_ROWS
         assert plan["grid"] == -(-plan["body"] // plan["tile"])
@@ -636,9 +660,12 @@ def test_plan_row_shapes_by_block_and_group(detfold_lib):
     for W in range(5, 17):
         n = 1_000_003
         one = df.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, W, n, CU, dict(rows, block=64 * W))
-        two = df.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, W, n, CU, dict(rows, block=64 * (-(-W // 2))))
+        two = df.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, W, n, CU, dict(rows, block=64 * _rows_waves(W, 2)))
         assert one["tile"] == 64 * (-(-W // 4)) and two["tile"] == 64
         assert two["grid"] == -(-two["body"] // 64)
+        if W in (13, 14):  # seven waves name no shape: the two-slot shape has eight
+            with pytest.raises(df.DetfoldError):
+                df.plan_fold_ranks(BASE, BASE + (1 << 34) + 4, W, n, CU, dict(rows, block=448))
     for W in (2, 3, 4):
         with pytest.raises(df.DetfoldError):
             df.plan_fold_ranks(BASE, BASE + (1 << 34), W, 1000, CU, dict(rows, block=64 * (-(-W // 2))))
@@ -667,12 +694,13 @@ def test_pair_link_refuses_stream_capture_before_any_call(detfold_lib, monkeypat
 
 
 def test_batch_plan_follows_the_pitch(detfold_lib):
-    # the shape rule reads the slot pitch: 625,002-float slots packed repeat no
-    # low 16 MiB of address (two slots per wave, runs of 8 tiles per XCD);
-    # padded to 2^22 floats (16 MiB) apart they do
+    # the shape rule reads the slot pitch: 625,002-float slots packed sit at
+    # alternating 16-byte phases and repeat no low 16 MiB of address (runs of
+    # 32 tiles per XCD); padded to 2^22 floats (16 MiB) apart they are
+    # co-aligned and repeat it (plain round-robin)
     df = detfold_lib
     packed = df.plan_fold_ranks_batch([(BASE, BASE + (1 << 34), 625_002)], 16, 256)
     padded = df.plan_fold_ranks_batch([(BASE, BASE + (1 << 34), 625_002, 1 << 22)], 16, 256)
-    assert (packed["block"], packed["tile"], packed["group"]) == (512, 64, 8)
+    assert (packed["block"], packed["tile"], packed["group"]) == (512, 64, 32)
     assert (padded["block"], padded["tile"], padded["group"]) == (512, 64, 1)
     assert packed["body"] == padded["body"] and packed["grid"] == padded["grid"]

@@ -35,9 +35,10 @@ def test_plan_kernel_names(detfold_lib):
     assert name(base, base + (1 << 34), 8, 1 << 24) == \
         "k_fold_rows<8,1,false> grid=32768 block=512 tile=128 xcd_group=1"
     assert name(base, base + (1 << 34), 8, 1 << 23).startswith("k_fold_rows<8,2,false>")
-    assert name(base, base + (1 << 34), 8, 10_000_000).endswith("block=512 tile=128 xcd_group=8")
+    assert name(base, base + (1 << 34), 8, 10_000_000).endswith("block=512 tile=128 xcd_group=32")
     assert name(base, base + (1 << 34), 7, 1 << 22).startswith("k_fold_rows<7,2,false> grid=16384 block=256")
-    assert name(base, base + (1 << 34) + 4, 7, 1 << 20).startswith("k_fold_rows<7,1,false> grid=2048 block=448")
+    assert name(base, base + (1 << 34) + 4, 7, 1 << 20).startswith("k_fold_rows<7,2,false> grid=4096 block=256")
+    assert name(base, base + (1 << 34), 14, 1 << 20).startswith("k_fold_rows<14,2,false> grid=4096 block=512")
     assert name(base, base + (1 << 34), 4, 100_000_000, True) == \
         "k_fold_rows<4,1,true> grid=390625 block=256 tile=64 xcd_group=8"
     assert name(base, base + (1 << 34) + 4, 16, 10_000_019).startswith("k_fold_rows<16,2,false> grid=39063 block=512")
