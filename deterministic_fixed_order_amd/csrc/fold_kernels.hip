@@ -514,10 +514,12 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
 // running sum stays in the thread's registers between passes, so each element
 // still sees the adds in strictly ascending slot order, one rounding each,
 // and is stored once at the end.
+// With a one-pass grid the tiles go to the XCDs in runs of `group` (xcd_tile).
 template <int WAVES, int SPW, int KIB, bool SCALED>
 __global__ __launch_bounds__(WAVES * 64) void k_fold_rows_wide(float *out, const float *s0,
                                                                const float *s1, int64_t stride, int w,
-                                                               int64_t len, int64_t head, float inv_w)
+                                                               int64_t len, int64_t head, float inv_w,
+                                                               int group)
 {
     constexpr int T = KIB * 64;  // groups per tile, at most one per thread
     static_assert(T <= WAVES * 64, "one group per thread");
@@ -533,7 +535,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_fold_rows_wide(float *out, const
     const uint32_t lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const uint32_t t = threadIdx.x;
-    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
+    const int64_t ntiles = (groups + T - 1) / T;
+    const bool one_pass = (int64_t)gridDim.x == ntiles;
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const int64_t tile = one_pass ? xcd_tile(b, ntiles, group) : b;
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;
@@ -897,7 +902,8 @@ int launch_plan(const Geometry &g, const detfold_plan &p, bool scaled, float inv
                                           : (const void *)k_fold_rows_wide<AW, AS, AK, false>)
                                 : (scaled ? (const void *)k_fold_rows_wide<kWideWaves, 1, kWideKiB, true>
                                           : (const void *)k_fold_rows_wide<kWideWaves, 1, kWideKiB, false>);
-        void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w};
+        int group = p.group;
+        void *args[] = {&out, &s0, &s1, &stride, &w, &len, &head, &inv_w, &group};
         e = launch(k, grid, block, args, stream, done, begin);
     } else if (p.path == DETFOLD_PATH_ROWS) {
         const int spw = rows_spw(w, p.block / 64);  // the plan's workgroup size names the shape

@@ -22,7 +22,14 @@ constexpr int kWideSlots = 16;     // slots per pass of the wide row body (W > k
 // Shapes of a pass of the wide row body: 16 waves x 1 slot x 4 KiB, or, when
 // every slot shares out's 16-byte phase, 8 waves x 2 slots x 1 KiB (measured
 // on MI355X at W = 24..64: 2.6-21.5% faster co-aligned, 2.7-5.5% slower with
-// shifted slots).
+// shifted slots).  Shifted slots whose length in bytes is a multiple of
+// kRepeatBytes take runs of 32 tiles per XCD, and the eight-wave shape too
+// where the last pass holds at least eight slots: +12% to +20% at W = 32
+// and 64 (W=32 x 2^22 at base+1: 5,370 -> 6,441 GB/s), +3% at W = 24; W = 17
+// in the eight-wave shape lost 7.7% (its second pass is one slot).  6
+// interleaved rounds each, bit-checked.  Elsewhere groups and the other
+// shape tie or move by a few percent either way (W = 17..64 at lengths 5e6
+// to 1.2e7), and the rule above stands.
 constexpr int kWideWaves = 16, kWideKiB = 4;
 constexpr int kWideAlignedWaves = 8, kWideAlignedKiB = 1;
 

@@ -59,21 +59,31 @@ int rows_slots_per_wave(const Geometry &g)
     return vector_legal(g) && slots_repeat(g) ? 2 : 1;
 }
 
+// Whether a wide fold (beyond 16 slots) takes the eight-wave pass shape: when
+// every slot shares out's phase, or when the slots repeat the low address bits
+// and the last pass holds at least half of 16 slots (a pass of a few slots
+// leaves most of the eight-wave shape's waves idle: W = 17 loses 7.7%).
+static bool wide_eight_waves(const Geometry &g)
+{
+    const int last = g.w % kWideSlots;
+    return vector_legal(g) || (slots_repeat(g) && (last == 0 || last >= kWideSlots / 2));
+}
+
 // Workgroup size and tile (16-byte groups) of the row bodies: one wave per
 // one or two slots up to 16 slots; beyond that, passes of 16 slots by
-// 16 waves (8 waves when every slot shares out's phase).
+// 16 waves, or 8 waves (wide_eight_waves).
 int rows_block(const Geometry &g)
 {
     if (g.w <= kMaxRowsW)
         return 64 * rows_waves(g.w, rows_slots_per_wave(g));
-    return 64 * (vector_legal(g) ? kWideAlignedWaves : kWideWaves);
+    return 64 * (wide_eight_waves(g) ? kWideAlignedWaves : kWideWaves);
 }
 
 int64_t rows_tile(const Geometry &g)
 {
     if (g.w <= kMaxRowsW)
         return (int64_t)rows_kib_per_wave(g.w, rows_slots_per_wave(g)) * 64;
-    return (int64_t)(vector_legal(g) ? kWideAlignedKiB : kWideKiB) * 64;
+    return (int64_t)(wide_eight_waves(g) ? kWideAlignedKiB : kWideKiB) * 64;
 }
 
 // The tile of the row-body shape a workgroup size names, or 0 if it names
@@ -102,10 +112,14 @@ int64_t rows_tile_for_block(const Geometry &g, int block)
 // phase, runs of kSlotGroupMid tiles per XCD (kSlotGroup at three slots);
 // co-aligned, plain round-robin where the slots repeat the low address bits,
 // else runs of kSlotGroupMid tiles from five to ten slots and of kSlotGroup
-// otherwise.  Separate slot buffers keep plain round-robin.
+// otherwise.  Beyond sixteen slots, runs of kSlotGroupMid for shifted slots
+// that repeat the low address bits, plain round-robin otherwise.  Separate
+// slot buffers keep plain round-robin.
 int rows_group(const Geometry &g, int block)
 {
     (void)block;
+    if (g.w > kMaxRowsW && !g.has_table)
+        return !vector_legal(g) && slots_repeat(g) ? kSlotGroupMid : 1;
     if (g.w < 3 || g.w > kMaxRowsW || g.has_table)
         return 1;
     if (!vector_legal(g))
@@ -202,8 +216,7 @@ int make_plan(const Geometry &g, int32_t cu_count, const detfold_launch *ovr, in
         p->unroll = 1;
         p->block = o.block ? o.block : rows_block(g);
         p->tile = rows_tile_for_block(g, p->block);
-        if (g.w <= kMaxRowsW)
-            p->group = o.group ? o.group : rows_group(g, p->block);
+        p->group = o.group ? o.group : rows_group(g, p->block);
     } else {
         p->unroll = policy == DETFOLD_POLICY_CACHED ? 1 : (o.unroll ? o.unroll : default_unroll(path));
         int block = o.block;

@@ -429,8 +429,8 @@ typedef struct detfold_launch {
     int32_t unroll; /* groups (vector) or elements (scalar) per thread per tile: 0 = default, 1, 2 or 4
                        (ROWS: 0 or 1) */
     int32_t policy; /* DETFOLD_POLICY_*: 0 = the entry point's own policy */
-    int32_t group;  /* ROWS, W <= 16, one pass: each XCD takes runs of this many neighbouring
-                       tiles (0 = the plan's choice, else a power of two up to 64; 1 = plain
+    int32_t group;  /* ROWS, one pass: each XCD takes runs of this many neighbouring tiles
+                       (0 = the plan's choice, else a power of two up to 64; 1 = plain
                        round-robin) */
 } detfold_launch;
 

@@ -46,9 +46,6 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
         if ((int64_t)p->head + 4 * p->body + p->tail != len)
             fail("head + body + tail != len", W, len);
     }
-    /* eight slots of a stacked arena: two slots per wave unless len is a multiple of 2^24;
-     * the other widths from five to sixteen: two when every slot shares out's 16-byte phase,
-     * an odd width's last wave streaming one */
     if (p->path == DETFOLD_PATH_ROWS && forced_block) {
         /* an override names the shape: the plan keeps it, with that shape's tile */
         const int64_t tile = W > 16 ? (forced_block == 1024 ? 256 : 64)
@@ -74,7 +71,11 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
         fail("row body with the wrong XCD group", W, len);
     /* two slots per wave: ceil(W/2) waves, eight at thirteen and fourteen slots */
     const int waves = W > 16 ? 0 : (spw == 2 && (W == 13 || W == 14)) ? 8 : (W + spw - 1) / spw;
-    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * waves : coaligned ? 512 : 1024))
+    if (p->path == DETFOLD_PATH_ROWS && W > 16 && p->group != (forced_group ? forced_group
+                                                              : !coaligned && repeat ? 32 : 1))
+        fail("wide row body with the wrong XCD group", W, len);
+    const int wide8 = coaligned || (repeat && (W % 16 == 0 || W % 16 >= 8));
+    if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * waves : wide8 ? 512 : 1024))
         fail("row body with the wrong workgroup size", W, len);
     if (p->path == DETFOLD_PATH_ROWS && W <= 16 && spw == 2 && p->tile != 64)
         fail("two-slot row body with the wrong tile", W, len);
