@@ -96,8 +96,12 @@ constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot len
 //    (W=16 x 2^22 at base+1: 4,950 -> 6,747 GB/s; W=9 x 3*2^22: +28%), +5%
 //    at W=8 x 2^24 at base+1 and a tie at W=16 x 2^24.  Shifted arenas whose
 //    slots do not repeat tie or gain up to 2.2% with runs of 32 against 8
-//    (the W=16 x 10,000,019 arena at base+1: +0.1% to +0.4%); three slots
-//    keep runs of 8 (runs of 32 lose up to 1.2%).
+//    (the W=16 x 10,000,019 arena at base+1: +0.1% to +0.4%), except at
+//    three and four slots, which keep runs of 8 there (W=4 x 1e8 at base+1:
+//    runs of 8 +2.6% over 32); shifted repeating arenas of three and four
+//    slots take runs of 32 too (W=3 x 2^23 at base+2: +10% over 8; W=4 x
+//    2^24 at base+1: +4.5% over plain round-robin).  Two-slot folds keep
+//    plain round-robin everywhere (groups tie or lose up to 4.6%).
 //  * Seven slots take two slots per wave on every stacked arena: one slot
 //    per wave means seven-wave workgroups, 28 of a CU's 32 wave slots
 //    (+3% to +6% at slot lengths 10^7 and 1.5*10^7).

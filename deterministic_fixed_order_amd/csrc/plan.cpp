@@ -109,8 +109,8 @@ int64_t rows_tile_for_block(const Geometry &g, int block)
 
 // XCD tile group of the row body (xcd_tile in fold_kernels.hip), for stacked
 // arenas of three to sixteen slots: with slots shifted from out's 16-byte
-// phase, runs of kSlotGroupMid tiles per XCD (kSlotGroup at three slots);
-// co-aligned, plain round-robin where the slots repeat the low address bits,
+// phase, runs of kSlotGroupMid tiles per XCD (kSlotGroup at three and four
+// slots that do not repeat the low address bits); co-aligned, plain round-robin where the slots repeat the low address bits,
 // else runs of kSlotGroupMid tiles from five to ten slots and of kSlotGroup
 // otherwise.  Beyond sixteen slots, runs of kSlotGroupMid for shifted slots
 // that repeat the low address bits, plain round-robin otherwise.  Separate
@@ -123,7 +123,7 @@ int rows_group(const Geometry &g, int block)
     if (g.w < 3 || g.w > kMaxRowsW || g.has_table)
         return 1;
     if (!vector_legal(g))
-        return g.w == 3 ? kSlotGroup : kSlotGroupMid;
+        return g.w <= 4 && !slots_repeat(g) ? kSlotGroup : kSlotGroupMid;
     if (slots_repeat(g))
         return 1;
     return g.w >= 5 && g.w <= 10 ? kSlotGroupMid : kSlotGroup;

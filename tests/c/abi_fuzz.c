@@ -57,7 +57,8 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
     /* slots per wave: eight slots one where len is a multiple of 2^24 or the
      * slots do not repeat the low 16 MiB of address, else two; seven and nine
      * to sixteen two; five and six two only co-aligned and repeating.  XCD
-     * group: shifted slots runs of 32 (8 at three slots); co-aligned plain
+     * group: shifted slots runs of 32 (8 at three and four slots that do not
+     * repeat); co-aligned plain
      * round-robin when repeating, else 32 from five to ten slots and 8 */
     const int repeat = len % ((int64_t)1 << 22) == 0;
     const int spw = (W < 5 || W > 16) ? 1
@@ -65,7 +66,7 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
                     : (W == 7 || W >= 9) ? 2
                     : (coaligned && repeat) ? 2 : 1;
     const int group = (W < 3 || W > 16) ? 1
-                      : !coaligned ? (W == 3 ? 8 : 32)
+                      : !coaligned ? (W <= 4 && !repeat ? 8 : 32)
                       : repeat ? 1 : (W >= 5 && W <= 10 ? 32 : 8);
     if (p->path == DETFOLD_PATH_ROWS && W <= 16 && p->group != (forced_group ? forced_group : group))
         fail("row body with the wrong XCD group", W, len);

@@ -155,9 +155,9 @@ def _rule_shape(W, n, coaligned):
     eight slots take one where n is a multiple of 2^24 or the slots do not
     repeat the address bits below 16 MiB, else two; seven and nine to sixteen
     take two; five and six take two only when co-aligned and repeating.  XCD
-    group: shifted slots take runs of 32 tiles (8 at three slots); co-aligned
-    ones plain round-robin when repeating, else runs of 32 from five to ten
-    slots and of 8 otherwise."""
+    group: shifted slots take runs of 32 tiles (8 at three and four slots that
+    do not repeat); co-aligned ones plain round-robin when repeating, else
+    runs of 32 from five to ten slots and of 8 otherwise."""
     repeat = (n * 4) % (1 << 24) == 0
     if W < 5 or W > 16:
         spw = 1
@@ -170,7 +170,7 @@ def _rule_shape(W, n, coaligned):
     if W < 3 or W > 16:
         group = 1
     elif not coaligned:
-        group = 8 if W == 3 else 32
+        group = 8 if (W <= 4 and not repeat) else 32
     elif repeat:
         group = 1
     else:
