@@ -347,18 +347,23 @@ def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_st
     call starts).  Two scrubs: writing the buffer and then reading it back
     (the cache is left holding clean lines), and writing it only (the cache
     is left holding dirty lines, whose write-back then competes with the
-    fold).  Every call is timed twice at once: by an event pair recorded
-    around it on the stream (launch and event latency included), and by the
-    start/stop events its own dispatch records (the kernel alone)."""
+    fold).  A third set has no scrub, only the host synchronization before
+    each call, so the device idles between folds: it separates what a launch
+    from idle costs from what the scrub leaves behind.  Every call is timed
+    twice at once: by an event pair recorded around it on the stream (launch
+    and event latency included), and by the start/stop events its own
+    dispatch records (the kernel alone)."""
     stream = timer.stream
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     gb = lambda ms: round(bytes_per_step / (ms * 1e-3) / 1e9, 2)
     res = {"calls": args.singles}
-    for key, read_back in (("write_then_read_scrub", True), ("write_scrub", False)):
+    for key, fill, read_back in (("write_then_read_scrub", True, True), ("write_scrub", True, False),
+                                 ("no_scrub", False, False)):
         pairs = timing_events(torch, stream, args.singles)
         outer, inner = [], []
         for i, (a, b) in enumerate(pairs):
-            scrub.fill_(float(i))
+            if fill:
+                scrub.fill_(float(i))
             if read_back:
                 scrub.amax()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -371,7 +376,7 @@ def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_st
             outer.append(e0.elapsed_time(e1))
             inner.append(a.elapsed_time(b))
         med_o, med_i = statistics.median(outer), statistics.median(inner)
-        log("single launches after a 1 GiB %s: event pair around the call median %.4f ms (%.1f GB/s), "
+        log("single launches, %s: event pair around the call median %.4f ms (%.1f GB/s), "
             "kernel alone median %.4f ms (%.1f GB/s)" % (key.replace("_", " "), med_o, gb(med_o), med_i,
                                                            gb(med_i)))
         res[key] = {"kernel_only_median_ms": round(med_i, 6), "kernel_only_best_ms": round(min(inner), 6),
@@ -382,17 +387,22 @@ def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_st
     torch.cuda.synchronize()
     res["note"] = ("kernel_only: start/stop events recorded by the fold's own dispatch; event_pair: events "
                    "recorded on the stream before and after the call; scrub: 1 GiB filled (and, in the "
-                   "first set, then read back with amax) before each call")
+                   "first set, then read back with amax) before each call; no_scrub: only the host "
+                   "synchronization between calls, the device idle")
     return res
 
 
 def settle(timer, step, target_ms=100.0):
     """Untimed calls for about target_ms, so that clocks that dropped while
     the device idled (host-side setup, the CPU oracle) are back up before a
-    timed region starts."""
+    timed region starts.  The queue is drained here: the first launches after
+    a drain of a thousand queued calls measured slow (about 40-80 us over a
+    20-step region), so the caller's warm-up calls, not its timed region,
+    come right after the drain."""
     ms = timer.region(step, 3) / 3
     for _ in range(min(2000, int(target_ms / max(ms, 1e-3)))):
         step()
+    timer.torch.cuda.synchronize()
 
 
 def bench_ceiling(args, torch, dev, timer, stacked, out):
