@@ -26,6 +26,13 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
+PAIR_CAPTURE_OFF = ("capturing the pair link into a HIP graph ended the test process with a segmentation "
+                    "fault inside hipStreamEndCapture, twice: first with the link's dispatch-recorded "
+                    "events under capture, then with plain launches and event records inside the capture "
+                    "and no wait on events recorded outside it.  The cause is not known, so the link "
+                    "refuses stream capture (DETFOLD_ECAPTURE) and these cases stay off")
+
+
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -278,9 +285,7 @@ def test_pair_all_reduce_beside_a_busy_stream(env):
     busy.synchronize()
 
 
-@pytest.mark.skip(reason="capturing the pair link into a HIP graph ended the test process with a "
-                         "segmentation fault inside hipStreamEndCapture; the cause is not known, so the "
-                         "link now refuses stream capture (DETFOLD_ECAPTURE) and this case stays off")
+@pytest.mark.skip(reason=PAIR_CAPTURE_OFF)
 @pytest.mark.parametrize("n", [4096, 65536])
 def test_pair_all_reduce_graph_replays(env, n):
     # One call captured in a HIP graph (both rank streams forked from the
@@ -288,6 +293,7 @@ def test_pair_all_reduce_graph_replays(env, n):
     # synchronizations between the replays: replay k must hold 2^(k-1) times
     # the sum on both ranks, bit for bit.
     df, torch, dev = env
+    _say("case: pair all-reduce captured into a graph, n=%d" % n)
     link = df.PairLink(n, device=dev)
     ha, hb = fold_inputs.vecf(n, 11 + n), fold_inputs.vecf(n, 77 + n)
     xa = torch.from_numpy(ha).to(dev)
@@ -303,6 +309,38 @@ def test_pair_all_reduce_graph_replays(env, n):
         _assert_bits(xa.cpu().numpy(), want, "rank 0 replay %d" % k)
         _assert_bits(xb.cpu().numpy(), want, "rank 1 replay %d" % k)
         want = oracle.fold_into(want, want)
+
+
+@pytest.mark.skip(reason=PAIR_CAPTURE_OFF)
+def test_pair_movement_graph_replays(env):
+    # A broadcast and an all-gather captured into one HIP graph, replayed
+    # three times with eager writes to every destination between replays:
+    # each replay must leave the bytes exactly (the events are graph edges).
+    df, torch, dev = env
+    span = 1027
+    _say("case: pair all-gather and broadcast captured into a graph, span=%d" % span)
+    link = df.PairLink(span, device=dev)
+    ha, hb = fold_inputs.vecf(span, 5), fold_inputs.vecf(span, 6)
+    xa = torch.from_numpy(ha).to(dev)
+    xb = torch.from_numpy(hb).to(dev)
+    f0 = torch.zeros(2 * span, dtype=torch.float32, device=dev)
+    f1 = torch.zeros(2 * span, dtype=torch.float32, device=dev)
+    d = torch.zeros(span, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        link.all_gather(xa, xb, f0, f1)
+        link.broadcast(1, xb, d)
+    want = np.concatenate([ha, hb])
+    for k in range(3):
+        f0.fill_(-1.0)
+        f1.fill_(-2.0)
+        d.fill_(-3.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        _assert_bits(f0.cpu().numpy(), want, "all-gather rank 0, replay %d" % k)
+        _assert_bits(f1.cpu().numpy(), want, "all-gather rank 1, replay %d" % k)
+        _assert_bits(d.cpu().numpy(), hb, "broadcast from rank 1, replay %d" % k)
 
 
 def test_pair_all_reduce_orders_against_the_current_stream(env):
