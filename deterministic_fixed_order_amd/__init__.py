@@ -402,9 +402,14 @@ class PairLink:
     Stream order: every call first makes both rank streams wait for the
     caller's current stream (so work already queued there on the tensors,
     such as the writes that produced them, comes first), and before it
-    returns makes the current stream wait for both rank streams (so later
-    work there, including the allocator's reuse of a freed tensor, comes
-    after).  Between the two the ranks run on their own streams.
+    returns makes the current stream wait for the events that mark the end of
+    the call's last work on each rank stream -- the ones the library's
+    dispatches record (``folded`` after an all-reduce, ``pushed`` after the
+    movement calls) -- so later work there, including the allocator's reuse
+    of a freed tensor, comes after.  One event recorded on the current
+    stream serves both rank streams, and the join records none: each
+    recorded event costs the host several microseconds.  Between the two the
+    ranks run on their own streams.
 
     The link cannot be captured into a HIP graph (the library returns
     ``ECAPTURE``); every call raises before touching the device while the
@@ -421,6 +426,9 @@ class PairLink:
         self.folded = [torch.cuda.Event(enable_timing=False) for _ in range(2)]
         for e in self.pushed + self.folded:
             e.record(self.streams[0])  # materialise the underlying event
+        # marks the caller's stream for both rank streams at each call's start
+        self._entry = torch.cuda.Event(enable_timing=False)
+        self._ranks = [self.streams[0]] if self.streams[1] == self.streams[0] else list(self.streams)
         torch.cuda.synchronize(dev)
         self.capacity = capacity
         self._c = PairLinkC()
@@ -437,13 +445,17 @@ class PairLink:
         if torch.cuda.is_current_stream_capturing():
             raise DetfoldError(ECAPTURE, "PairLink")
         cur = torch.cuda.current_stream(self.device)
-        for s in self.streams:
-            s.wait_stream(cur)
+        self._entry.record(cur)
+        for s in self._ranks:
+            s.wait_event(self._entry)
         return cur
 
-    def _join(self, cur) -> None:
-        for s in self.streams:
-            cur.wait_stream(s)
+    @staticmethod
+    def _join(cur, marks) -> None:
+        """The current stream waits for the events that end the call's work on
+        the rank streams."""
+        for e in marks:
+            cur.wait_event(e)
 
     def all_reduce(self, x0, x1) -> None:
         _f32_device(x0, "x0")
@@ -453,7 +465,7 @@ class PairLink:
         cur = self._fork()
         _check(load().detfold_pair_all_reduce(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
                                               x0.numel()), "pair_all_reduce")
-        self._join(cur)
+        self._join(cur, self.folded)  # each rank's fold is its stream's last work
 
     def broadcast(self, root: int, src, dst) -> None:
         """``dst`` (rank ``1 - root``) becomes a byte copy of ``src`` (rank ``root``)."""
@@ -464,7 +476,7 @@ class PairLink:
         cur = self._fork()
         _check(load().detfold_pair_broadcast(ctypes.byref(self._c), int(root), src.data_ptr(),
                                              dst.data_ptr(), src.numel()), "pair_broadcast")
-        self._join(cur)
+        self._join(cur, [self.pushed[int(root)]])  # the copy; the other stream only waits for it
 
     def all_gather(self, x0, x1, f0, f1) -> None:
         """``f0`` and ``f1`` (2 * span floats) both become ``[x0 | x1]``."""
@@ -476,7 +488,7 @@ class PairLink:
         cur = self._fork()
         _check(load().detfold_pair_all_gather(ctypes.byref(self._c), x0.data_ptr(), x1.data_ptr(),
                                               f0.data_ptr(), f1.data_ptr(), span), "pair_all_gather")
-        self._join(cur)
+        self._join(cur, self.pushed)  # each rank's copy; after it a stream only waits
 
 
 class OneShotLink:
