@@ -105,6 +105,11 @@ constexpr int64_t kOneSlotAlign = (int64_t)1 << 24;  // floats; stacked slot len
 //  * Seven slots take two slots per wave on every stacked arena: one slot
 //    per wave means seven-wave workgroups, 28 of a CU's 32 wave slots
 //    (+3% to +6% at slot lengths 10^7 and 1.5*10^7).
+//  * Separate slot buffers (fold_slots) shifted from out's phase take the
+//    same shapes and groups as shifted stacked slots that do not repeat:
+//    +3% to +21% at W = 4..16 on buffers of 2^22 and 10^7 floats (W=12 x
+//    2^22 two elements off: 5,326 -> 6,422 GB/s; W=7: +18.8%), a tie at W=3,
+//    -2.3% at W=16 x 2^24.  Co-aligned tables keep their shapes.
 constexpr int64_t kRepeatBytes = (int64_t)1 << 24;
 constexpr int kSlotGroup = 8;
 constexpr int kSlotGroupMid = 32;

@@ -38,8 +38,9 @@ bool slots_repeat(const Geometry &g)
 }
 
 // Slots each wave of the row body streams.
-//  * Separate slot buffers (a table): two for eight slots and for five to
-//    sixteen slots that all share out's 16-byte phase, else one.
+//  * Separate slot buffers (a table): two from five slots up when every slot
+//    shares out's 16-byte phase, and from seven up when some slot does not;
+//    else one.
 //  * Stacked arenas of eight slots: one where the slot length is a multiple
 //    of kOneSlotAlign or the slots do not repeat the low address bits, else
 //    two.
@@ -51,7 +52,7 @@ int rows_slots_per_wave(const Geometry &g)
     if (g.w > kMaxRowsW || g.w < 5)
         return 1;
     if (g.has_table)
-        return g.w == 8 || vector_legal(g) ? 2 : 1;
+        return vector_legal(g) || g.w >= 7 ? 2 : 1;
     if (g.w == 8)
         return g.stride % kOneSlotAlign == 0 || !slots_repeat(g) ? 1 : 2;
     if (g.w == 7 || g.w >= 9)
@@ -114,13 +115,16 @@ int64_t rows_tile_for_block(const Geometry &g, int block)
 // else runs of kSlotGroupMid tiles from five to ten slots and of kSlotGroup
 // otherwise.  Beyond sixteen slots, runs of kSlotGroupMid for shifted slots
 // that repeat the low address bits, plain round-robin otherwise.  Separate
-// slot buffers keep plain round-robin.
+// slot buffers: shifted ones as shifted stacked slots that do not repeat,
+// co-aligned ones plain round-robin.
 int rows_group(const Geometry &g, int block)
 {
     (void)block;
     if (g.w > kMaxRowsW && !g.has_table)
         return !vector_legal(g) && slots_repeat(g) ? kSlotGroupMid : 1;
-    if (g.w < 3 || g.w > kMaxRowsW || g.has_table)
+    if (g.has_table)
+        return vector_legal(g) || g.w < 3 || g.w > kMaxRowsW ? 1 : (g.w <= 4 ? kSlotGroup : kSlotGroupMid);
+    if (g.w < 3 || g.w > kMaxRowsW)
         return 1;
     if (!vector_legal(g))
         return g.w <= 4 && !slots_repeat(g) ? kSlotGroup : kSlotGroupMid;
