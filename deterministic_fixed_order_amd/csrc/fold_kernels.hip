@@ -446,9 +446,22 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_batch(Bat
 // barrier) before it writes any of them, and workgroups own disjoint tiles;
 // the head and tail elements are read, folded and written back by one thread
 // each.  Every byte of every slot is read once and written once.
+//
+// With a one-pass grid the tiles go to the XCDs in runs of `group`
+// (xcd_tile).  A slot's run that does not start on a 128-byte line shares
+// its first and last line with the neighbouring tiles' runs of that slot, and
+// those partial lines are written back through the L2 (no write-through) so
+// that the neighbours' halves can meet there; runs on whole lines keep the
+// write-through stores.  Measured on MI355X (5 interleaved rounds,
+// bit-checked) against write-through everywhere: +18% at W=8 x 10^7 with
+// every arena one element off a line, +29% with the arenas at four different
+// 16-byte phases, +4.5-5% at W=16; line-aligned arenas unchanged (write-back
+// stores there lose 6-8%).  The fold's own output keeps write-through even off
+// a line: write-back lost 4-8% there, its output being a small share of the
+// traffic.
 template <int W, int SPW>
 __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotTable slots, int64_t len,
-                                                                int64_t head)
+                                                                int64_t head, int group)
 {
     constexpr int LPW = RowsShape<W, SPW>::LPW, T = RowsShape<W, SPW>::T;
     constexpr int NT = RowsShape<W, SPW>::WAVES * 64;  // threads per workgroup
@@ -470,7 +483,10 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int64_t tile = blockIdx.x; tile * T < groups; tile += gridDim.x) {
+    const int64_t ntiles = (groups + T - 1) / T;
+    const bool one_pass = (int64_t)gridDim.x == ntiles;
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const int64_t tile = one_pass ? xcd_tile(b, ntiles, group) : b;
         const int64_t g0 = tile * T;
         const int64_t cnt = groups - g0 < T ? groups - g0 : T;
         const int64_t e0 = head + 4 * g0;
@@ -494,11 +510,16 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
             if (r >= hi)
                 break;  // this wave has fewer slots
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots.p[r] + e0, (uint32_t)(cnt * 16));
+            const bool on_line = ((uintptr_t)(slots.p[r] + e0) & 127) == 0;  // uniform per wave
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {
                 const uint32_t g = (uint32_t)(u * 64) + lane;
-                if (g < (uint32_t)cnt)
-                    bstore<Aux<kStream>::store>(rows[0][g], rs, g * 16u);
+                if (g < (uint32_t)cnt) {
+                    if (on_line)
+                        bstore<Aux<kStream>::store>(rows[0][g], rs, g * 16u);
+                    else
+                        bstore<Aux<kCached>::store>(rows[0][g], rs, g * 16u);
+                }
             }
         }
         __syncthreads();  // row 0 is read before the next tile refills the rows
@@ -812,7 +833,7 @@ rows_batch_kernel_t pick_rows_batch(int32_t w, int spw)
     }
 }
 
-typedef void (*rows_all_kernel_t)(SlotTable, int64_t, int64_t);
+typedef void (*rows_all_kernel_t)(SlotTable, int64_t, int64_t, int);
 
 rows_all_kernel_t pick_rows_all(int32_t w, int spw)
 {
@@ -955,7 +976,8 @@ int launch_rows_all(const Geometry &g, const detfold_plan &p, void *stream)
     for (int32_t r = 0; r < g.w; ++r)
         slots.p[r] = reinterpret_cast<const float *>(g.table[r]);
     int64_t len = g.len, head = p.head;
-    void *args[] = {&slots, &len, &head};
+    int group = p.group;
+    void *args[] = {&slots, &len, &head, &group};
     return launch(reinterpret_cast<const void *>(k), dim3((unsigned)p.grid), dim3((unsigned)p.block), args,
                   static_cast<hipStream_t>(stream), nullptr) == hipSuccess
                ? DETFOLD_OK
