@@ -5,7 +5,9 @@ Headline workload: fold_ranks over a stacked [8][16777216] float32 arena
 (64 MiB per slot), slot r = vecf(2^24, 1000 + r), into a separate output.
 One step is one fold_ranks call; it moves (W+1)*len*4 = 603,979,776 bytes
 (W slots read, one output written).  The inputs are resident in HBM before
-the timed region starts.
+the timed region starts, and each step writes the next of 8 outputs in turn
+(512 MiB, twice the memory-side cache), so that every step's stores reach HBM;
+the line also gives the rate into one reused output for comparison.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -44,6 +46,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+MEMORY_SIDE_CACHE_BYTES = 256 << 20  # MI355X's last-level cache on the memory side of the fabric
 METRIC = "fold GB/s (W+1 bufs moved) and % HBM peak at W=8, 64 MiB/slot; 16 KiB latency"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fold_w8_64mib_hbm_counters.md")
 LIB_SOURCES = sorted(glob.glob(os.path.join(ROOT, "deterministic_fixed_order_amd", "csrc", "*.hip")) +
@@ -172,11 +175,50 @@ def make_workload(name, torch, dev, want_host=False):
     return host, stacked, out, W, n, inv_w
 
 
-def fold_step(df, out, stacked, inv_w):
-    """One fold_ranks (or fold_ranks_scaled) call on the current stream."""
+def output_set(torch, out):
+    """`out` and more buffers like it, together at least twice the memory-side
+    cache.  A timed region writes each step into the next of them in turn, so
+    no line an earlier step wrote can still sit in that cache when a step
+    writes it, and every step's stores reach HBM.  Folded into one output
+    back to back, the cache takes part of each step's writes: with the
+    stores written through, W=8 x 2^24 ran at 7,050-7,072 GB/s into one or
+    two outputs, 6,922 into four (256 MiB) and 6,668 into eight."""
+    count = max(2, -(-2 * MEMORY_SIDE_CACHE_BYTES // (out.numel() * 4)))
+    return [out] + [torch.empty_like(out) for _ in range(count - 1)]
+
+
+def rotating(bufs, call):
+    """A step that calls call(b) with the next b of bufs in turn."""
+    state = [0]
+
+    def step():
+        b = bufs[state[0] % len(bufs)]
+        state[0] += 1
+        call(b)
+    return step
+
+
+def fold_call(df, stacked, inv_w):
+    """call(out): one fold_ranks (or fold_ranks_scaled) into out on the current stream."""
     if inv_w is None:
-        return lambda: df.fold_ranks(out, stacked)
-    return lambda: df.fold_ranks_scaled(out, stacked, inv_w)
+        return lambda o: df.fold_ranks(o, stacked)
+    return lambda o: df.fold_ranks_scaled(o, stacked, inv_w)
+
+
+def fold_step(df, outs, stacked, inv_w):
+    """One fold per call, into the next buffer of outs in turn."""
+    return rotating(outs, fold_call(df, stacked, inv_w))
+
+
+def write_all(torch, outs, call):
+    """call(o) once for every o in outs, then wait: every buffer holds a result."""
+    for o in outs:
+        call(o)
+    torch.cuda.synchronize()
+
+
+def all_equal(torch, outs, ref):
+    return all(bool(torch.equal(o.view(torch.int32), ref.view(torch.int32))) for o in outs)
 
 
 def timing_events(torch, stream, count):
@@ -192,25 +234,29 @@ def timing_events(torch, stream, count):
     return pairs
 
 
-def kernel_only_ms(torch, df, stream, out, stacked, inv_w, calls):
+def kernel_only_ms(torch, df, stream, outs, stacked, inv_w, calls):
     """Durations (ms) of `calls` back-to-back fold kernels, each timed by
-    events its own dispatch records (detfold_fold_ranks_timed)."""
+    events its own dispatch records (detfold_fold_ranks_timed), each into the
+    next buffer of outs in turn."""
     pairs = timing_events(torch, stream, calls)
-    for a, b in pairs:
-        df.fold_ranks_timed(out, stacked, a, b, scaled=inv_w is not None,
+    for i, (a, b) in enumerate(pairs):
+        df.fold_ranks_timed(outs[i % len(outs)], stacked, a, b, scaled=inv_w is not None,
                             inv_w=inv_w if inv_w is not None else 1.0)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in pairs]
 
 
-def oracle_check(host, inv_w, out):
-    """The whole GPU output against the CPU oracle, bit for bit."""
+def oracle_check(host, inv_w, outs):
+    """The first output against the CPU oracle bit for bit, and every other
+    output of the rotation against the first."""
     import numpy as np
     import oracle
+    import torch
     want = oracle.fold_stacked(host) if inv_w is None else \
         oracle.fold_stacked_scaled(host, np.float32(inv_w))
-    got = out.cpu().numpy()
-    return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
+    got = outs[0].cpu().numpy()
+    return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32))) and \
+        all_equal(torch, outs[1:], outs[0])
 
 
 def traffic_for(name):
@@ -244,19 +290,23 @@ def bench_fold(args, torch, df, dev):
     bytes_per_step = (W + 1) * n * 4
     stream = torch.cuda.current_stream(dev)
     timer = Timer(torch, stream)
-    step = fold_step(df, out, stacked, inv_w)
+    outs = output_set(torch, out)
+    step = fold_step(df, outs, stacked, inv_w)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("warmup done (%d steps); timing %d steps of %s" % (args.warmup, args.steps, name))
+    log("warmup done (%d steps); timing %d steps of %s, each into the next of %d outputs"
+        % (args.warmup, args.steps, name, len(outs)))
     ms_total = timer.region(step, args.steps)
     ms_per_step = ms_total / args.steps
     gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log("timed region: %.3f ms per step, %.1f GB/s" % (ms_per_step, gbs))
-    kern = kernel_only_ms(torch, df, stream, out, stacked, inv_w, args.steps)
+    kern = kernel_only_ms(torch, df, stream, outs, stacked, inv_w, args.steps)
     kern_avg = statistics.mean(kern)
     log("kernel-only (dispatch-recorded events), %d back-to-back launches: average %.4f ms, "
         "median %.4f ms" % (len(kern), kern_avg, statistics.median(kern)))
+    reused = bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step)
+    write_all(torch, outs, fold_call(df, stacked, inv_w))
 
     singles = bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step) \
         if args.singles > 0 else None
@@ -277,14 +327,16 @@ def bench_fold(args, torch, df, dev):
         "dtype": "f32",
         "data": "synthetic (seeded xorshift64 generators, resident in HBM)",
         "config": {"workload": WORKLOAD_NAMES[name], "W": W, "len": n,
-                   "bytes_per_step": bytes_per_step, "parallelism": "single GPU"},
+                   "bytes_per_step": bytes_per_step, "parallelism": "single GPU",
+                   "outputs_rotated": len(outs)},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "output_reused": reused,
     }
     result["roofline"] = roofline(gbs, ms_per_step, bytes_per_step,
                                   kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
                                   traffic_for(name), kern_avg, attainable)
     if args.alternate and inv_w is None:
-        result["alternating_arenas"] = bench_alternating(args, torch, df, dev, timer, stacked, out,
+        result["alternating_arenas"] = bench_alternating(args, torch, df, dev, timer, stacked, outs,
                                                          bytes_per_step)
     if singles:
         result["scrubbed_single_launch"] = singles
@@ -296,11 +348,11 @@ def bench_fold(args, torch, df, dev):
     if args.workload == "w16" and args.owner_shards:
         result["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step)
+        result["cpu_baseline"] = cpu_baseline(args, host, inv_w, outs, W, n, bytes_per_step)
     else:
-        result["bit_exact_vs_oracle"] = oracle_check(host, inv_w, out)
+        result["bit_exact_vs_oracle"] = oracle_check(host, inv_w, outs)
     if args.workload == "w8" and args.secondary:
-        del host, stacked, out, step
+        del host, stacked, out, outs, step
         torch.cuda.empty_cache()
         result["secondary"] = {w: bench_secondary(args, torch, df, dev, w) for w in ("w4", "w16")}
     return result
@@ -315,20 +367,24 @@ def bench_secondary(args, torch, df, dev, name):
     bytes_per_step = (W + 1) * n * 4
     stream = torch.cuda.current_stream(dev)
     timer = Timer(torch, stream)
-    step = fold_step(df, out, stacked, inv_w)
+    outs = output_set(torch, out)
+    step = fold_step(df, outs, stacked, inv_w)
     settle(timer, step)
     for _ in range(args.warmup):
         step()
     ms = timer.region(step, args.steps) / args.steps
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
-    kern = kernel_only_ms(torch, df, stream, out, stacked, inv_w, args.steps)
-    exact = oracle_check(host, inv_w, out)
+    kern = kernel_only_ms(torch, df, stream, outs, stacked, inv_w, args.steps)
+    reused = bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step)
+    write_all(torch, outs, fold_call(df, stacked, inv_w))
+    exact = oracle_check(host, inv_w, outs)
     log("%s: %.4f ms per step, %.1f GB/s (%.1f%% of peak); kernel-only average %.4f ms; bit-exact vs "
         "the oracle: %s" % (name, ms, gbs, 100 * gbs / HBM_PEAK_GBS, statistics.mean(kern), exact))
     if not exact:
         raise RuntimeError("%s: the GPU fold differs from the oracle" % name)
     res = {"workload": WORKLOAD_NAMES[name], "W": W, "len": n, "bytes_per_step": bytes_per_step,
-           "steps": args.steps, "ms_per_step": round(ms, 6), "GBps": round(gbs, 2),
+           "outputs_rotated": len(outs), "steps": args.steps, "ms_per_step": round(ms, 6),
+           "GBps": round(gbs, 2), "output_reused": reused,
            "kernel_only_median_ms": round(statistics.median(kern), 6),
            "roofline": roofline(gbs, ms, bytes_per_step,
                                 kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
@@ -336,9 +392,23 @@ def bench_secondary(args, torch, df, dev, name):
            "bit_exact_vs_oracle": exact}
     if name == "w16" and args.owner_shards:
         res["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
-    del host, stacked, out
+    del host, stacked, out, outs
     torch.cuda.empty_cache()
     return res
+
+
+def bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step):
+    """The same fold into one output back to back, for comparison with the
+    rotation: the memory-side cache can then hold lines of the previous step's
+    output when a step writes it."""
+    step = fold_step(df, [out], stacked, inv_w)
+    for _ in range(args.warmup):
+        step()
+    ms = timer.region(step, args.steps) / args.steps
+    gbs = bytes_per_step / (ms * 1e-3) / 1e9
+    log("one output reused: %.4f ms per step, %.1f GB/s" % (ms, gbs))
+    return {"ms_per_step": round(ms, 6), "GBps": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "every step into the same output; not the headline, whose outputs rotate"}
 
 
 def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step):
@@ -479,42 +549,40 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     scratch = [_torch.empty((W, l), dtype=_torch.float32, device=out.device) for _, l in shards]
     for (s, l), sc in zip(shards, scratch):
         sc.copy_(stacked[:, s:s + l])
-    out_sep, out_one = _torch.empty_like(out), _torch.empty_like(out)
-    views_sep = [out_sep[s:s + l] for s, l in shards]
-    views_one = [out_one[s:s + l] for s, l in shards]
+    outs = output_set(_torch, _torch.empty_like(out))
+    views = [[o[s:s + l] for s, l in shards] for o in outs]
+    in_place = [stacked[:, s:s + l] for s, l in shards]  # row stride n: no gather at all
 
-    def separate():
-        for o, sc in zip(views_sep, scratch):
+    def separate(v):
+        for o, sc in zip(v, scratch):
             df.fold_ranks(o, sc)
 
-    def one_launch():
-        df.fold_ranks_batch(views_one, scratch)
+    def one_launch(v):
+        df.fold_ranks_batch(v, scratch)
 
-    in_place = [stacked[:, s:s + l] for s, l in shards]  # row stride n: no gather at all
-    out_arena = _torch.empty_like(out)
-    views_arena = [out_arena[s:s + l] for s, l in shards]
-
-    def one_launch_from_arena():
-        df.fold_ranks_batch(views_arena, in_place)
+    def one_launch_from_arena(v):
+        df.fold_ranks_batch(v, in_place)
     moved = (W + 1) * n * 4
-    res = {"shards": W, "shard_len_max": max(l for _, l in shards),
+    res = {"shards": W, "shard_len_max": max(l for _, l in shards), "outputs_rotated": len(outs),
            "note": "shards gathered once by device copies (untimed); per step every shard fold, "
-                   "as separate launches and as one batched launch"}
-    for key, fn in (("separate_launches", separate), ("one_launch", one_launch),
-                    ("one_launch_shards_read_from_the_arena", one_launch_from_arena)):
+                   "as separate launches and as one batched launch, into the next output of the "
+                   "rotation"}
+    for key, call in (("separate_launches", separate), ("one_launch", one_launch),
+                      ("one_launch_shards_read_from_the_arena", one_launch_from_arena)):
+        for o in outs:
+            o.fill_(float("nan"))  # what this variant does not write fails the check below
+        fn = rotating(views, call)
         settle(timer, fn)
         for _ in range(args.warmup):
             fn()
         ms = timer.region(fn, args.steps) / args.steps
         gbs = moved / (ms * 1e-3) / 1e9
-        res[key] = {"ms_per_set": round(ms, 5), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    _torch.cuda.synchronize()
-    same_sep = bool(_torch.equal(out_sep.view(_torch.int32), out.view(_torch.int32)))
-    same_one = bool(_torch.equal(out_one.view(_torch.int32), out.view(_torch.int32)))
-    same_arena = bool(_torch.equal(out_arena.view(_torch.int32), out.view(_torch.int32)))
-    res["one_launch_shards_read_from_the_arena"]["bits_equal_whole_fold"] = same_arena
-    res["separate_launches"]["bits_equal_whole_fold"] = same_sep
-    res["one_launch"]["bits_equal_whole_fold"] = same_one
+        write_all(_torch, views, call)
+        res[key] = {"ms_per_set": round(ms, 5), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "bits_equal_whole_fold": all_equal(_torch, outs, out)}
+    same_sep = res["separate_launches"]["bits_equal_whole_fold"]
+    same_one = res["one_launch"]["bits_equal_whole_fold"]
+    same_arena = res["one_launch_shards_read_from_the_arena"]["bits_equal_whole_fold"]
     res["one_launch"]["traffic"] = traffic_for("w16_shards_one_launch")
     log("owner shards: %d shard folds of about %d elements: %d launches %.4f ms per set (%.1f GB/s), one "
         "batched launch %.4f ms (%.1f GB/s); bits equal to the whole fold: %s / %s"
@@ -528,35 +596,37 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     return res
 
 
-def bench_alternating(args, torch, df, dev, timer, stacked, out, bytes_per_step):
+def bench_alternating(args, torch, df, dev, timer, stacked, outs, bytes_per_step):
     """The same fold, alternating between the arena and a separately allocated
-    copy of it (with its own output): each step's operands were last touched
-    two folds earlier, with a whole other arena read in between, so the
-    memory-side last-level cache can hold none of them when the step starts.
-    A rate close to the back-to-back one shows the latter is not cache-fed."""
+    copy of it, each step into the next output of the rotation: each step's
+    slots were last read two folds earlier, with a whole other arena read in
+    between, so the memory-side last-level cache can hold none of them when
+    the step starts.  A rate close to the headline's shows that its reads are
+    not cache-fed."""
     stacked2 = stacked.clone()
-    out2 = torch.empty_like(out)
-    pair = [(out, stacked), (out2, stacked2)]
+    arenas = [stacked, stacked2]
     state = [0]
 
     def step():
-        o, s = pair[state[0] & 1]
+        i = state[0]
         state[0] += 1
-        df.fold_ranks(o, s)
+        df.fold_ranks(outs[i % len(outs)], arenas[i & 1])
 
     for _ in range(4):
         step()
     torch.cuda.synchronize()
     steps = args.steps - (args.steps & 1)
     ms = timer.region(step, steps) / steps
-    torch.cuda.synchronize()
-    same = bool(torch.equal(out.view(torch.int32), out2.view(torch.int32)))
-    del stacked2, out2
+    ref = outs[0].clone()
+    write_all(torch, outs, lambda o: df.fold_ranks(o, stacked2))
+    same = all_equal(torch, outs, ref)
+    del stacked2
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
     log("alternating two arenas: %.3f ms per step, %.1f GB/s (outputs equal: %s)" % (ms, gbs, same))
     return {"ms_per_step": round(ms, 6), "GBps": round(gbs, 2), "steps": steps,
             "outputs_equal": same,
-            "note": "two separately allocated copies of the arena, folded in turn"}
+            "note": "two separately allocated copies of the arena, folded in turn, each step into the "
+                    "next output of the rotation"}
 
 
 def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
@@ -666,7 +736,7 @@ def launch_floor(torch, dev, timer, k_graph) -> float:
     return ms
 
 
-def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
+def cpu_baseline(args, host, inv_w, outs, W, n, bytes_per_step):
     """The CPU oracle on the same host arrays, single-threaded, repeated for a
     bounded time; its result is also checked bit for bit against the GPU's."""
     import numpy as np
@@ -684,8 +754,9 @@ def cpu_baseline(args, host, inv_w, out, W, n, bytes_per_step):
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    bit_exact = bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
+    got = outs[0].cpu().numpy()
+    bit_exact = bool(np.array_equal(got.view(np.uint32), want.view(np.uint32))) and \
+        all_equal(torch, outs[1:], outs[0])
     log("cpu oracle: %d runs, median %.3f s (%.2f GB/s); GPU output bit-exact: %s"
         % (len(times), med, bytes_per_step / med / 1e9, bit_exact))
     threads = min(len(os.sched_getaffinity(0)), 16)
@@ -970,14 +1041,13 @@ def bench_one_shot(torch, df, dev, shot, xa, xb):
 
 
 def sweep(args, torch, df, dev):
-    """Launch-geometry sweep of the headline fold (all results bit-checked
-    against the default launch's output)."""
-    import numpy as np
-
+    """Launch-geometry sweep of the headline fold, outputs rotating (all
+    results bit-checked against the default launch's output)."""
     host, stacked, out, W, n, _ = make_workload("w8", torch, dev)
     timer = Timer(torch, torch.cuda.current_stream(dev))
     df.fold_ranks(out, stacked)
-    ref = out.cpu().numpy().view(np.uint32).copy()
+    ref = out.clone()
+    outs = output_set(torch, out)
     bytes_per_step = (W + 1) * n * 4
     configs = [(df.PATH_ROWS, df.POLICY_STREAM, 64 * W, 1, grid) for grid in (0, 512, 1024, 2048, 4096)]
     for policy in (df.POLICY_STREAM, df.POLICY_CACHED):
@@ -990,14 +1060,17 @@ def sweep(args, torch, df, dev):
         for c in configs:
             path, policy, block, unroll, grid = c
 
-            def step():
-                df.fold_ranks_ex(out, stacked, path=path, block=block, grid=grid, unroll=unroll,
+            def call(o):
+                df.fold_ranks_ex(o, stacked, path=path, block=block, grid=grid, unroll=unroll,
                                  policy=policy)
+            step = rotating(outs, call)
             for _ in range(3):
                 step()
             samples[c].append(timer.region(step, 20) / 20)
-            if rnd == 0 and not np.array_equal(out.cpu().numpy().view(np.uint32), ref):
-                raise AssertionError("sweep configuration %s changed the bits" % (c,))
+            if rnd == 0:
+                write_all(torch, outs, call)
+                if not all_equal(torch, outs, ref):
+                    raise AssertionError("sweep configuration %s changed the bits" % (c,))
     rows = []
     for c in configs:
         ms = statistics.median(samples[c])

@@ -57,9 +57,12 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 // Cache-policy operand of the gfx950 buffer instructions: bit 0 = sc0,
 // bit 1 = nt, bit 4 = sc1.
 template <int POL> struct Aux {
-    static constexpr int load = POL == kStream ? 2 : 0;    // nt
-    static constexpr int store = POL == kStream ? 17 : 0;  // sc0 sc1
+    static constexpr int load = POL == kStream ? 2 : 0;   // nt
+    static constexpr int store = POL == kStream ? 2 : 0;  // nt
 };
+// Written through to system scope (sc0 sc1): the fused round's stores of
+// whole lines back into its arenas.
+constexpr int kStoreThrough = 17;
 
 // Raw buffer descriptor word 3 for gfx9-family parts (32-bit data format,
 // no swizzle); the range check is num_records in bytes.
@@ -451,14 +454,14 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_batch(Bat
 // (xcd_tile).  A slot's run that does not start on a 128-byte line shares
 // its first and last line with the neighbouring tiles' runs of that slot, and
 // those partial lines are written back through the L2 (no write-through) so
-// that the neighbours' halves can meet there; runs on whole lines keep the
-// write-through stores.  Measured on MI355X (5 interleaved rounds,
+// that the neighbours' halves can meet there; runs on whole lines are
+// written through (sc0 sc1).  Measured on MI355X (5 interleaved rounds,
 // bit-checked) against write-through everywhere: +18% at W=8 x 10^7 with
 // every arena one element off a line, +29% with the arenas at four different
 // 16-byte phases, +4.5-5% at W=16; line-aligned arenas unchanged (write-back
-// stores there lose 6-8%).  The fold's own output keeps write-through even off
-// a line: write-back lost 4-8% there, its output being a small share of the
-// traffic.
+// stores there lose 6-8%).  The non-temporal stores of the other stream
+// kernels lose 1.1% here against write-through (W=8 x 2^24, line-aligned):
+// the round writes back into the arenas it has just read.
 template <int W, int SPW>
 __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotTable slots, int64_t len,
                                                                 int64_t head, int group)
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(rows_waves(W, SPW) * 64) void k_fold_rows_all(SlotT
                 const uint32_t g = (uint32_t)(u * 64) + lane;
                 if (g < (uint32_t)cnt) {
                     if (on_line)
-                        bstore<Aux<kStream>::store>(rows[0][g], rs, g * 16u);
+                        bstore<kStoreThrough>(rows[0][g], rs, g * 16u);
                     else
                         bstore<Aux<kCached>::store>(rows[0][g], rs, g * 16u);
                 }

@@ -417,7 +417,7 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
 #define DETFOLD_PATH_ROWS 3   /* LDS row body, W >= 2, any alignment, streaming only        */
 
 #define DETFOLD_POLICY_DEFAULT 0
-#define DETFOLD_POLICY_STREAM 1 /* non-temporal loads, write-through stores */
+#define DETFOLD_POLICY_STREAM 1 /* non-temporal loads and stores */
 #define DETFOLD_POLICY_CACHED 2 /* no cache hints (available with unroll 1 only) */
 
 typedef struct detfold_launch {

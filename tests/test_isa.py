@@ -9,7 +9,8 @@ gfx950 assembly it produced:
   v_fmaak/v_fmamk, mixed-precision forms, packed FP32);
 * every kernel descriptor keeps f32 denormals (.amdhsa_float_denorm_mode_32 3);
 * no writes through the scalar data cache;
-* the LDS row kernels load with the nt and lds bits and store with sc0 sc1;
+* the LDS row kernels load with the nt and lds bits and store with nt, and
+  the fused round writes whole lines through with sc0 sc1;
 * the default kernels spill nothing to scratch.
 """
 import glob
@@ -59,6 +60,7 @@ def test_row_kernels_stream_through_lds(isa):
     loads = re.findall(r"^\s*buffer_load_dwordx4\s+.*\blds\b.*$", isa, re.M)
     assert loads and all(" nt" in l for l in loads)
     stores = re.findall(r"^\s*buffer_store_dwordx4\s.*$", isa, re.M)
+    assert any(l.rstrip().endswith(" nt") for l in stores)
     assert any("sc0 sc1" in l for l in stores)
 
 
