@@ -597,36 +597,43 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
 
 
 def bench_alternating(args, torch, df, dev, timer, stacked, outs, bytes_per_step):
-    """The same fold, alternating between the arena and a separately allocated
-    copy of it, each step into the next output of the rotation: each step's
-    slots were last read two folds earlier, with a whole other arena read in
-    between, so the memory-side last-level cache can hold none of them when
-    the step starts.  A rate close to the headline's shows that its reads are
-    not cache-fed."""
+    """Whether the headline's reads are cache-fed: regions of the headline's
+    own steps (one arena) interleaved with regions whose steps alternate
+    between the arena and a separately allocated copy of it, every step into
+    the next output of the rotation.  With two arenas each step's slots were
+    last read two folds earlier, a whole other arena (twice the memory-side
+    cache) read in between, so that cache holds none of them; equal rates
+    show that the one-arena rate is not fed by it either.  Interleaving gives
+    both the same device state (clocks, temperature)."""
     stacked2 = stacked.clone()
     arenas = [stacked, stacked2]
     state = [0]
 
-    def step():
+    def two():
         i = state[0]
         state[0] += 1
         df.fold_ranks(outs[i % len(outs)], arenas[i & 1])
 
-    for _ in range(4):
-        step()
-    torch.cuda.synchronize()
-    steps = args.steps - (args.steps & 1)
-    ms = timer.region(step, steps) / steps
+    one = fold_step(df, outs, stacked, None)
+    steps = max(2, args.steps - (args.steps & 1))
+    samples = {"one_arena": [], "two_arenas": []}
+    for _ in range(3):
+        for key, fn in (("one_arena", one), ("two_arenas", two)):
+            for _ in range(4):
+                fn()
+            samples[key].append(timer.region(fn, steps) / steps)
     ref = outs[0].clone()
     write_all(torch, outs, lambda o: df.fold_ranks(o, stacked2))
     same = all_equal(torch, outs, ref)
     del stacked2
-    gbs = bytes_per_step / (ms * 1e-3) / 1e9
-    log("alternating two arenas: %.3f ms per step, %.1f GB/s (outputs equal: %s)" % (ms, gbs, same))
-    return {"ms_per_step": round(ms, 6), "GBps": round(gbs, 2), "steps": steps,
-            "outputs_equal": same,
-            "note": "two separately allocated copies of the arena, folded in turn, each step into the "
-                    "next output of the rotation"}
+    res = {"steps_per_region": steps, "regions_each": 3, "outputs_equal": same,
+           "note": "regions of one arena and of two alternating arenas, interleaved; outputs rotate"}
+    for key, v in samples.items():
+        ms = statistics.median(v)
+        res[key] = {"ms_per_step": round(ms, 6), "GBps": round(bytes_per_step / (ms * 1e-3) / 1e9, 2)}
+    log("one arena %.1f GB/s, two alternating arenas %.1f GB/s (interleaved regions; outputs equal: %s)"
+        % (res["one_arena"]["GBps"], res["two_arenas"]["GBps"], same))
+    return res
 
 
 def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:

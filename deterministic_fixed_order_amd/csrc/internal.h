@@ -27,11 +27,15 @@ constexpr int kWideSlots = 16;     // slots per pass of the wide row body (W > k
 // where the last pass holds at least eight slots: +12% to +20% at W = 32
 // and 64 (W=32 x 2^22 at base+1: 5,370 -> 6,441 GB/s), +3% at W = 24; W = 17
 // in the eight-wave shape lost 7.7% (its second pass is one slot).  6
-// interleaved rounds each, bit-checked.  Elsewhere groups and the other
-// shape tie or move by a few percent either way (W = 17..64 at lengths 5e6
-// to 1.2e7), and the rule above stands.
+// interleaved rounds each, bit-checked.  Shifted slots that do not repeat
+// keep the sixteen-wave shape and take runs of kWideShiftedGroup tiles per
+// XCD: +0.4% to +2.1% over plain round-robin at six arenas of W = 17..48,
+// lengths 5e6 to 1.2e7, one to three elements off (6 interleaved rounds,
+// outputs rotating past the memory-side cache, bit-checked), never a loss;
+// runs of 8 gained +0.3% to +2.1%, of 32 -0.4% to +2.0%.
 constexpr int kWideWaves = 16, kWideKiB = 4;
 constexpr int kWideAlignedWaves = 8, kWideAlignedKiB = 1;
+constexpr int kWideShiftedGroup = 16;
 
 // KiB of one slot each wave of the LDS row body streams per tile: ceil(W/4)
 // for W >= 3, 8 for W = 2.  Measured on MI355X over W = 2..16 and 1/2/4/8 KiB

@@ -111,17 +111,19 @@ int64_t rows_tile_for_block(const Geometry &g, int block)
 // XCD tile group of the row body (xcd_tile in fold_kernels.hip), for stacked
 // arenas of three to sixteen slots: with slots shifted from out's 16-byte
 // phase, runs of kSlotGroupMid tiles per XCD (kSlotGroup at three and four
-// slots that do not repeat the low address bits); co-aligned, plain round-robin where the slots repeat the low address bits,
-// else runs of kSlotGroupMid tiles from five to ten slots and of kSlotGroup
-// otherwise.  Beyond sixteen slots, runs of kSlotGroupMid for shifted slots
-// that repeat the low address bits, plain round-robin otherwise.  Separate
-// slot buffers: shifted ones as shifted stacked slots that do not repeat,
-// co-aligned ones plain round-robin.
+// slots that do not repeat the low address bits); co-aligned, plain
+// round-robin where the slots repeat the low address bits, else runs of
+// kSlotGroupMid tiles from five to ten slots and of kSlotGroup otherwise.
+// Beyond sixteen slots, shifted slots take runs of kSlotGroupMid where they
+// repeat the low address bits and of kWideShiftedGroup where they do not;
+// co-aligned ones plain round-robin.  Separate slot buffers: shifted ones as
+// shifted stacked slots that do not repeat, co-aligned ones plain
+// round-robin.
 int rows_group(const Geometry &g, int block)
 {
     (void)block;
     if (g.w > kMaxRowsW && !g.has_table)
-        return !vector_legal(g) && slots_repeat(g) ? kSlotGroupMid : 1;
+        return vector_legal(g) ? 1 : (slots_repeat(g) ? kSlotGroupMid : kWideShiftedGroup);
     if (g.has_table)
         return vector_legal(g) || g.w < 3 || g.w > kMaxRowsW ? 1 : (g.w <= 4 ? kSlotGroup : kSlotGroupMid);
     if (g.w < 3 || g.w > kMaxRowsW)

@@ -58,8 +58,8 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
      * slots do not repeat the low 16 MiB of address, else two; seven and nine
      * to sixteen two; five and six two only co-aligned and repeating.  XCD
      * group: shifted slots runs of 32 (8 at three and four slots that do not
-     * repeat); co-aligned plain
-     * round-robin when repeating, else 32 from five to ten slots and 8 */
+     * repeat; beyond sixteen slots 16 where they do not repeat); co-aligned
+     * plain round-robin when repeating, else 32 from five to ten slots and 8 */
     const int repeat = len % ((int64_t)1 << 22) == 0;
     const int spw = (W < 5 || W > 16) ? 1
                     : W == 8 ? ((len % ((int64_t)1 << 24) == 0 || !repeat) ? 1 : 2)
@@ -73,7 +73,7 @@ static void check_plan(const detfold_plan *p, int32_t W, int64_t len, int coalig
     /* two slots per wave: ceil(W/2) waves, eight at thirteen and fourteen slots */
     const int waves = W > 16 ? 0 : (spw == 2 && (W == 13 || W == 14)) ? 8 : (W + spw - 1) / spw;
     if (p->path == DETFOLD_PATH_ROWS && W > 16 && p->group != (forced_group ? forced_group
-                                                              : !coaligned && repeat ? 32 : 1))
+                                                              : coaligned ? 1 : repeat ? 32 : 16))
         fail("wide row body with the wrong XCD group", W, len);
     const int wide8 = coaligned || (repeat && (W % 16 == 0 || W % 16 >= 8));
     if (p->path == DETFOLD_PATH_ROWS && p->block != (W <= 16 ? 64 * waves : wide8 ? 512 : 1024))

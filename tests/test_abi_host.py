@@ -510,15 +510,15 @@ def test_plan_wide_rows(detfold_lib, W, n):
     # 64-group tiles when out and every slot share one 16-byte phase, or when
     # the slots repeat the low 16 MiB of address and the last pass holds at
     # least 8 slots, else 16 waves x 1 slot x 4 KiB over 256-group tiles;
-    # shifted repeating slots take runs of 32 tiles per XCD, every other wide
-    # arena plain round-robin
+    # shifted slots take runs of tiles per XCD (32 where they repeat, else
+    # 16), co-aligned wide arenas plain round-robin
     repeat = (n * 4) % (1 << 24) == 0 and (W % 16 == 0 or W % 16 >= 8)
     for out, stacked in ((BASE, BASE + (1 << 36)), (BASE + 4, BASE + (1 << 36) + 12)):
         aligned = out % 16 == stacked % 16 and n % 4 == 0
         p = detfold_lib.plan_fold_ranks(out, stacked, W, n, CU)
         assert p["path"] == detfold_lib.PATH_ROWS
         assert (p["block"], p["tile"], p["unroll"]) == ((512, 64, 1) if aligned or repeat else (1024, 256, 1))
-        assert p["group"] == (32 if (n * 4) % (1 << 24) == 0 and not aligned else 1)
+        assert p["group"] == (1 if aligned else 32 if (n * 4) % (1 << 24) == 0 else 16)
         assert p["grid"] == max(1, -(-p["body"] // p["tile"]))
         assert p["head"] + 4 * p["body"] + p["tail"] == n
     p = detfold_lib.plan_fold_ranks(BASE + 4, BASE + (1 << 36) + 12, W, n, CU,
