@@ -305,6 +305,7 @@ def bench_fold(args, torch, df, dev):
     kern_avg = statistics.mean(kern)
     log("kernel-only (dispatch-recorded events), %d back-to-back launches: average %.4f ms, "
         "median %.4f ms" % (len(kern), kern_avg, statistics.median(kern)))
+    sustained = bench_sustained(args, timer, step, bytes_per_step)
     reused = bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step)
     write_all(torch, outs, fold_call(df, stacked, inv_w))
 
@@ -330,6 +331,7 @@ def bench_fold(args, torch, df, dev):
                    "bytes_per_step": bytes_per_step, "parallelism": "single GPU",
                    "outputs_rotated": len(outs)},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "sustained": sustained,
         "output_reused": reused,
     }
     result["roofline"] = roofline(gbs, ms_per_step, bytes_per_step,
@@ -375,6 +377,7 @@ def bench_secondary(args, torch, df, dev, name):
     ms = timer.region(step, args.steps) / args.steps
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
     kern = kernel_only_ms(torch, df, stream, outs, stacked, inv_w, args.steps)
+    sustained = bench_sustained(args, timer, step, bytes_per_step)
     reused = bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step)
     write_all(torch, outs, fold_call(df, stacked, inv_w))
     exact = oracle_check(host, inv_w, outs)
@@ -384,7 +387,7 @@ def bench_secondary(args, torch, df, dev, name):
         raise RuntimeError("%s: the GPU fold differs from the oracle" % name)
     res = {"workload": WORKLOAD_NAMES[name], "W": W, "len": n, "bytes_per_step": bytes_per_step,
            "outputs_rotated": len(outs), "steps": args.steps, "ms_per_step": round(ms, 6),
-           "GBps": round(gbs, 2), "output_reused": reused,
+           "GBps": round(gbs, 2), "sustained": sustained, "output_reused": reused,
            "kernel_only_median_ms": round(statistics.median(kern), 6),
            "roofline": roofline(gbs, ms, bytes_per_step,
                                 kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
@@ -395,6 +398,20 @@ def bench_secondary(args, torch, df, dev, name):
     del host, stacked, out, outs
     torch.cuda.empty_cache()
     return res
+
+
+def bench_sustained(args, timer, step, bytes_per_step):
+    """The headline's step over one long region right after the headline's
+    (--sustained-steps, about 0.2 s at W=8): the rate under continuous load,
+    which the device's power and thermal management can hold below that of a
+    short region after a pause."""
+    if args.sustained_steps <= 0:
+        return None
+    ms = timer.region(step, args.sustained_steps) / args.sustained_steps
+    gbs = bytes_per_step / (ms * 1e-3) / 1e9
+    log("sustained, %d steps: %.4f ms per step, %.1f GB/s" % (args.sustained_steps, ms, gbs))
+    return {"steps": args.sustained_steps, "ms_per_step": round(ms, 6), "GBps": round(gbs, 2),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step):
@@ -1301,6 +1318,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["join", "round", "pair", "procs"],
                     default="w8")
     ap.add_argument("--singles", type=int, default=50, help="scrubbed single-launch samples")
+    ap.add_argument("--sustained-steps", type=int, default=2000,
+                    help="steps of the long region after the headline's (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true")

@@ -44,3 +44,22 @@ def test_plan_kernel_names(detfold_lib):
     assert name(base, base + (1 << 34) + 4, 16, 10_000_019).startswith("k_fold_rows<16,2,false> grid=39063 block=512")
     assert name(base, base + (1 << 34), 32, 1 << 20).startswith("k_fold_rows_wide<8,2,1,false>")
     assert name(base, base + (1 << 34) + 4, 32, 1 << 20).startswith("k_fold_rows_wide<16,1,4,false>")
+
+
+def test_output_set_spans_twice_the_memory_side_cache():
+    import torch
+    for n, count in ((1 << 24, 8), (100_000_000, 2), (10_000_019, 14), (8_000_001, 17), (4096, 32768)):
+        out = torch.empty(0).new_empty((n,), device="meta")
+        outs = bench.output_set(torch, out)
+        assert len(outs) == count and outs[0] is out
+        assert len(outs) * n * 4 >= 2 * bench.MEMORY_SIDE_CACHE_BYTES
+        assert (len(outs) - 1) * n * 4 < 2 * bench.MEMORY_SIDE_CACHE_BYTES or len(outs) == 2
+        assert all(o.shape == out.shape and o.dtype == out.dtype for o in outs)
+
+
+def test_rotating_step_takes_the_buffers_in_turn():
+    seen = []
+    step = bench.rotating(["a", "b", "c"], seen.append)
+    for _ in range(7):
+        step()
+    assert seen == ["a", "b", "c", "a", "b", "c", "a"]
