@@ -407,9 +407,9 @@ int detfold_shard_plan(int64_t n, int32_t world, int64_t *start, int64_t *length
  *   SCALAR  (otherwise) each thread loads 4 bytes of every slot directly.
  *
  * Cache policy: the bandwidth path (fold_ranks, fold_ranks_scaled, and
- * fold_into above 8 MiB per buffer) streams: loads carry the non-temporal
- * hint and stores are written through the L2.  fold_into at or below 8 MiB
- * per buffer uses no hints, since the folded result is read again soon.
+ * fold_into above 8 MiB per buffer) streams: loads and stores carry the
+ * non-temporal hint.  fold_into at or below 8 MiB per buffer uses no hints,
+ * since the folded result is read again soon.
  */
 #define DETFOLD_PATH_AUTO 0
 #define DETFOLD_PATH_VECTOR 1 /* direct body, 16-byte loads (out and every slot co-aligned) */
