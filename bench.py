@@ -5,9 +5,11 @@ Headline workload: fold_ranks over a stacked [8][16777216] float32 arena
 (64 MiB per slot), slot r = vecf(2^24, 1000 + r), into a separate output.
 One step is one fold_ranks call; it moves (W+1)*len*4 = 603,979,776 bytes
 (W slots read, one output written).  The inputs are resident in HBM before
-the timed region starts, and each step writes the next of 8 outputs in turn
-(512 MiB, twice the memory-side cache), so that every step's stores reach HBM;
-the line also gives the rate into one reused output for comparison.
+the timed region starts.  Each step folds the next of 3 copies of the arena
+into the next of 8 outputs (1 GiB of other arena copies between two reads of
+one copy, 512 MiB of outputs: four and two times the memory-side cache), so
+that no step finds its operands in that cache; the line's cache_controls
+give the rates with one arena and with every operand reused, interleaved.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -187,27 +189,43 @@ def output_set(torch, out):
     return [out] + [torch.empty_like(out) for _ in range(count - 1)]
 
 
-def rotating(bufs, call):
-    """A step that calls call(b) with the next b of bufs in turn."""
+def arena_set(torch, stacked, offset):
+    """`stacked` and copies of it, each in an allocation of its own at the same
+    element offset (so every copy keeps the arena's 16-byte phases), enough of
+    them that at least 1 GiB of the other copies -- four times the
+    memory-side cache -- is read between two reads of any one copy.  A
+    timed region folds the copies in turn, so no step's slots can still sit
+    in that cache from an earlier step.  Folding one arena over and over, the
+    cache fed 1.1-1.7% of the W=8 x 2^24 rate and 1.3-1.4% at W=16 x
+    10,000,019; nothing at W=4 x 1e8, whose arena is six times the cache."""
+    W, n = stacked.shape
+    count = 1 + max(1, -(-4 * MEMORY_SIDE_CACHE_BYTES // (W * n * 4)))
+    copies = [stacked]
+    for _ in range(count - 1):
+        alloc = torch.empty(W * n + offset, dtype=stacked.dtype, device=stacked.device)
+        copy = alloc[offset:].view(W, n)
+        copy.copy_(stacked)
+        copies.append(copy)
+    return copies
+
+
+def fold_call(df, inv_w):
+    """call(out, stacked): one fold_ranks (or fold_ranks_scaled) on the current stream."""
+    if inv_w is None:
+        return lambda o, s: df.fold_ranks(o, s)
+    return lambda o, s: df.fold_ranks_scaled(o, s, inv_w)
+
+
+def fold_step(df, outs, arenas, inv_w):
+    """One fold per call: call i folds arenas[i % A] into outs[i % R]."""
+    call = fold_call(df, inv_w)
     state = [0]
 
     def step():
-        b = bufs[state[0] % len(bufs)]
+        i = state[0]
         state[0] += 1
-        call(b)
+        call(outs[i % len(outs)], arenas[i % len(arenas)])
     return step
-
-
-def fold_call(df, stacked, inv_w):
-    """call(out): one fold_ranks (or fold_ranks_scaled) into out on the current stream."""
-    if inv_w is None:
-        return lambda o: df.fold_ranks(o, stacked)
-    return lambda o: df.fold_ranks_scaled(o, stacked, inv_w)
-
-
-def fold_step(df, outs, stacked, inv_w):
-    """One fold per call, into the next buffer of outs in turn."""
-    return rotating(outs, fold_call(df, stacked, inv_w))
 
 
 def write_all(torch, outs, call):
@@ -234,14 +252,14 @@ def timing_events(torch, stream, count):
     return pairs
 
 
-def kernel_only_ms(torch, df, stream, outs, stacked, inv_w, calls):
+def kernel_only_ms(torch, df, stream, outs, arenas, inv_w, calls):
     """Durations (ms) of `calls` back-to-back fold kernels, each timed by
-    events its own dispatch records (detfold_fold_ranks_timed), each into the
-    next buffer of outs in turn."""
+    events its own dispatch records (detfold_fold_ranks_timed), call i
+    folding arenas[i % A] into outs[i % R] as the timed steps do."""
     pairs = timing_events(torch, stream, calls)
     for i, (a, b) in enumerate(pairs):
-        df.fold_ranks_timed(outs[i % len(outs)], stacked, a, b, scaled=inv_w is not None,
-                            inv_w=inv_w if inv_w is not None else 1.0)
+        df.fold_ranks_timed(outs[i % len(outs)], arenas[i % len(arenas)], a, b,
+                            scaled=inv_w is not None, inv_w=inv_w if inv_w is not None else 1.0)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in pairs]
 
@@ -290,24 +308,27 @@ def bench_fold(args, torch, df, dev):
     bytes_per_step = (W + 1) * n * 4
     stream = torch.cuda.current_stream(dev)
     timer = Timer(torch, stream)
+    arenas = arena_set(torch, stacked, WORKLOADS[name][5])
     outs = output_set(torch, out)
-    step = fold_step(df, outs, stacked, inv_w)
+    step = fold_step(df, outs, arenas, inv_w)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("warmup done (%d steps); timing %d steps of %s, each into the next of %d outputs"
-        % (args.warmup, args.steps, name, len(outs)))
+    log("warmup done (%d steps); timing %d steps of %s, folding %d copies of the arena in turn, "
+        "each into the next of %d outputs" % (args.warmup, args.steps, name, len(arenas), len(outs)))
     ms_total = timer.region(step, args.steps)
     ms_per_step = ms_total / args.steps
     gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log("timed region: %.3f ms per step, %.1f GB/s" % (ms_per_step, gbs))
-    kern = kernel_only_ms(torch, df, stream, outs, stacked, inv_w, args.steps)
+    kern = kernel_only_ms(torch, df, stream, outs, arenas, inv_w, args.steps)
     kern_avg = statistics.mean(kern)
     log("kernel-only (dispatch-recorded events), %d back-to-back launches: average %.4f ms, "
         "median %.4f ms" % (len(kern), kern_avg, statistics.median(kern)))
     sustained = bench_sustained(args, timer, step, bytes_per_step)
-    reused = bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step)
-    write_all(torch, outs, fold_call(df, stacked, inv_w))
+    controls = bench_cache_controls(args, df, timer, outs, arenas, inv_w, bytes_per_step) \
+        if args.controls else None
+    call = fold_call(df, inv_w)
+    write_all(torch, outs, lambda o: [call(o, a) for a in arenas])
 
     singles = bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step) \
         if args.singles > 0 else None
@@ -329,17 +350,14 @@ def bench_fold(args, torch, df, dev):
         "data": "synthetic (seeded xorshift64 generators, resident in HBM)",
         "config": {"workload": WORKLOAD_NAMES[name], "W": W, "len": n,
                    "bytes_per_step": bytes_per_step, "parallelism": "single GPU",
-                   "outputs_rotated": len(outs)},
+                   "arena_copies_rotated": len(arenas), "outputs_rotated": len(outs)},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "sustained": sustained,
-        "output_reused": reused,
+        "cache_controls": controls,
     }
     result["roofline"] = roofline(gbs, ms_per_step, bytes_per_step,
                                   kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
                                   traffic_for(name), kern_avg, attainable)
-    if args.alternate and inv_w is None:
-        result["alternating_arenas"] = bench_alternating(args, torch, df, dev, timer, stacked, outs,
-                                                         bytes_per_step)
     if singles:
         result["scrubbed_single_launch"] = singles
     if ceiling:
@@ -348,13 +366,13 @@ def bench_fold(args, torch, df, dev):
     if args.workload == "w8" and not args.no_latency:
         result["latency_16KiB"] = bench_join(args, torch, df, dev, timer)
     if args.workload == "w16" and args.owner_shards:
-        result["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
+        result["owner_shards"] = bench_owner_shards(args, torch, df, timer, arenas, out, W, n)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, host, inv_w, outs, W, n, bytes_per_step)
     else:
         result["bit_exact_vs_oracle"] = oracle_check(host, inv_w, outs)
     if args.workload == "w8" and args.secondary:
-        del host, stacked, out, outs, step
+        del host, stacked, out, outs, arenas, step
         torch.cuda.empty_cache()
         result["secondary"] = {w: bench_secondary(args, torch, df, dev, w) for w in ("w4", "w16")}
     return result
@@ -369,33 +387,37 @@ def bench_secondary(args, torch, df, dev, name):
     bytes_per_step = (W + 1) * n * 4
     stream = torch.cuda.current_stream(dev)
     timer = Timer(torch, stream)
+    arenas = arena_set(torch, stacked, WORKLOADS[name][5])
     outs = output_set(torch, out)
-    step = fold_step(df, outs, stacked, inv_w)
+    step = fold_step(df, outs, arenas, inv_w)
     settle(timer, step)
     for _ in range(args.warmup):
         step()
     ms = timer.region(step, args.steps) / args.steps
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
-    kern = kernel_only_ms(torch, df, stream, outs, stacked, inv_w, args.steps)
+    kern = kernel_only_ms(torch, df, stream, outs, arenas, inv_w, args.steps)
     sustained = bench_sustained(args, timer, step, bytes_per_step)
-    reused = bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step)
-    write_all(torch, outs, fold_call(df, stacked, inv_w))
+    controls = bench_cache_controls(args, df, timer, outs, arenas, inv_w, bytes_per_step) \
+        if args.controls else None
+    call = fold_call(df, inv_w)
+    write_all(torch, outs, lambda o: [call(o, a) for a in arenas])
     exact = oracle_check(host, inv_w, outs)
     log("%s: %.4f ms per step, %.1f GB/s (%.1f%% of peak); kernel-only average %.4f ms; bit-exact vs "
         "the oracle: %s" % (name, ms, gbs, 100 * gbs / HBM_PEAK_GBS, statistics.mean(kern), exact))
     if not exact:
         raise RuntimeError("%s: the GPU fold differs from the oracle" % name)
     res = {"workload": WORKLOAD_NAMES[name], "W": W, "len": n, "bytes_per_step": bytes_per_step,
-           "outputs_rotated": len(outs), "steps": args.steps, "ms_per_step": round(ms, 6),
-           "GBps": round(gbs, 2), "sustained": sustained, "output_reused": reused,
+           "arena_copies_rotated": len(arenas), "outputs_rotated": len(outs), "steps": args.steps,
+           "ms_per_step": round(ms, 6), "GBps": round(gbs, 2), "sustained": sustained,
+           "cache_controls": controls,
            "kernel_only_median_ms": round(statistics.median(kern), 6),
            "roofline": roofline(gbs, ms, bytes_per_step,
                                 kernel_name(df, torch, dev, out, stacked, W, n, inv_w is not None),
                                 traffic_for(name), statistics.mean(kern)),
            "bit_exact_vs_oracle": exact}
     if name == "w16" and args.owner_shards:
-        res["owner_shards"] = bench_owner_shards(args, torch, df, timer, stacked, out, W, n)
-    del host, stacked, out, outs
+        res["owner_shards"] = bench_owner_shards(args, torch, df, timer, arenas, out, W, n)
+    del host, stacked, out, outs, arenas
     torch.cuda.empty_cache()
     return res
 
@@ -414,19 +436,30 @@ def bench_sustained(args, timer, step, bytes_per_step):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def bench_output_reused(args, torch, df, timer, out, stacked, inv_w, bytes_per_step):
-    """The same fold into one output back to back, for comparison with the
-    rotation: the memory-side cache can then hold lines of the previous step's
-    output when a step writes it."""
-    step = fold_step(df, [out], stacked, inv_w)
-    for _ in range(args.warmup):
-        step()
-    ms = timer.region(step, args.steps) / args.steps
-    gbs = bytes_per_step / (ms * 1e-3) / 1e9
-    log("one output reused: %.4f ms per step, %.1f GB/s" % (ms, gbs))
-    return {"ms_per_step": round(ms, 6), "GBps": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "note": "every step into the same output; not the headline, whose outputs rotate"}
-
+def bench_cache_controls(args, df, timer, outs, arenas, inv_w, bytes_per_step):
+    """What the rotation keeps out of the headline: regions of the headline's
+    own step (arena copies and outputs in turn) interleaved with regions that
+    fold one arena into the rotating outputs, and one arena into one output
+    (every operand reused), three regions each, so that all three see the same
+    device state (clocks, temperature, what ran before)."""
+    call = fold_call(df, inv_w)
+    forms = {"rotating": fold_step(df, outs, arenas, inv_w),
+             "one_arena": fold_step(df, outs, arenas[:1], inv_w),
+             "one_arena_one_output": lambda: call(outs[0], arenas[0])}
+    samples = {k: [] for k in forms}
+    for _ in range(3):
+        for key, fn in forms.items():
+            for _ in range(4):
+                fn()
+            samples[key].append(timer.region(fn, args.steps) / args.steps)
+    res = {"regions_each": 3, "steps_per_region": args.steps,
+           "note": "interleaved regions; rotating is the headline's step"}
+    for key, v in samples.items():
+        ms = statistics.median(v)
+        res[key] = {"ms_per_step": round(ms, 6), "GBps": round(bytes_per_step / (ms * 1e-3) / 1e9, 2)}
+    log("cache controls: rotating %.1f GB/s, one arena %.1f GB/s, one arena into one output %.1f GB/s"
+        % (res["rotating"]["GBps"], res["one_arena"]["GBps"], res["one_arena_one_output"]["GBps"]))
+    return res
 
 def bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step):
     """Single launches, each after a 1 GiB scrub (more than four times the
@@ -552,7 +585,7 @@ def device_info(torch, dev):
     return info
 
 
-def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
+def bench_owner_shards(args, torch, df, timer, arenas, out, W, n):
     """The owner-shard form of the offset arena: each of the W owners' shards
     is gathered once (untimed, device copies of the W slices) into a [W][l_p]
     scratch; then per step all W shard folds run into one output at the
@@ -560,41 +593,50 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     fold_ranks_batch launch; and, with no gather, one launch whose jobs read
     the owners' shards in place from the arena (row stride len).  Each must
     equal the whole-arena fold bit for bit.  Same algorithmic bytes as the
-    whole fold."""
+    whole fold.  As in the whole fold, the steps take the arena copies (and
+    their gathered shards) and the outputs in turn."""
     import torch as _torch
     shards = df.shard_plan(n, W)
-    scratch = [_torch.empty((W, l), dtype=_torch.float32, device=out.device) for _, l in shards]
-    for (s, l), sc in zip(shards, scratch):
-        sc.copy_(stacked[:, s:s + l])
+    scratch = []  # per arena copy, its W gathered shards
+    for a in arenas:
+        sc = [_torch.empty((W, l), dtype=_torch.float32, device=out.device) for _, l in shards]
+        for (s, l), buf in zip(shards, sc):
+            buf.copy_(a[:, s:s + l])
+        scratch.append(sc)
+    in_place = [[a[:, s:s + l] for s, l in shards] for a in arenas]  # row stride n: no gather
     outs = output_set(_torch, _torch.empty_like(out))
     views = [[o[s:s + l] for s, l in shards] for o in outs]
-    in_place = [stacked[:, s:s + l] for s, l in shards]  # row stride n: no gather at all
 
-    def separate(v):
-        for o, sc in zip(v, scratch):
+    def separate(v, src):
+        for o, sc in zip(v, src):
             df.fold_ranks(o, sc)
 
-    def one_launch(v):
-        df.fold_ranks_batch(v, scratch)
-
-    def one_launch_from_arena(v):
-        df.fold_ranks_batch(v, in_place)
+    def one_launch(v, src):
+        df.fold_ranks_batch(v, src)
     moved = (W + 1) * n * 4
     res = {"shards": W, "shard_len_max": max(l for _, l in shards), "outputs_rotated": len(outs),
+           "arena_copies_rotated": len(arenas),
            "note": "shards gathered once by device copies (untimed); per step every shard fold, "
-                   "as separate launches and as one batched launch, into the next output of the "
-                   "rotation"}
-    for key, call in (("separate_launches", separate), ("one_launch", one_launch),
-                      ("one_launch_shards_read_from_the_arena", one_launch_from_arena)):
+                   "as separate launches and as one batched launch, from the next arena copy into "
+                   "the next output of the rotation"}
+    for key, call, srcs in (("separate_launches", separate, scratch), ("one_launch", one_launch, scratch),
+                            ("one_launch_shards_read_from_the_arena", one_launch, in_place)):
         for o in outs:
             o.fill_(float("nan"))  # what this variant does not write fails the check below
-        fn = rotating(views, call)
+        state = [0]
+
+        def fn():
+            i = state[0]
+            state[0] += 1
+            call(views[i % len(views)], srcs[i % len(srcs)])
         settle(timer, fn)
         for _ in range(args.warmup):
             fn()
         ms = timer.region(fn, args.steps) / args.steps
         gbs = moved / (ms * 1e-3) / 1e9
-        write_all(_torch, views, call)
+        for k, v in enumerate(views):
+            call(v, srcs[k % len(srcs)])
+        _torch.cuda.synchronize()
         res[key] = {"ms_per_set": round(ms, 5), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "bits_equal_whole_fold": all_equal(_torch, outs, out)}
     same_sep = res["separate_launches"]["bits_equal_whole_fold"]
@@ -611,47 +653,6 @@ def bench_owner_shards(args, torch, df, timer, stacked, out, W, n):
     if not (same_sep and same_one and same_arena):
         raise RuntimeError("the owner-shard folds differ from the whole-arena fold")
     return res
-
-
-def bench_alternating(args, torch, df, dev, timer, stacked, outs, bytes_per_step):
-    """Whether the headline's reads are cache-fed: regions of the headline's
-    own steps (one arena) interleaved with regions whose steps alternate
-    between the arena and a separately allocated copy of it, every step into
-    the next output of the rotation.  With two arenas each step's slots were
-    last read two folds earlier, a whole other arena (twice the memory-side
-    cache) read in between, so that cache holds none of them; equal rates
-    show that the one-arena rate is not fed by it either.  Interleaving gives
-    both the same device state (clocks, temperature)."""
-    stacked2 = stacked.clone()
-    arenas = [stacked, stacked2]
-    state = [0]
-
-    def two():
-        i = state[0]
-        state[0] += 1
-        df.fold_ranks(outs[i % len(outs)], arenas[i & 1])
-
-    one = fold_step(df, outs, stacked, None)
-    steps = max(2, args.steps - (args.steps & 1))
-    samples = {"one_arena": [], "two_arenas": []}
-    for _ in range(3):
-        for key, fn in (("one_arena", one), ("two_arenas", two)):
-            for _ in range(4):
-                fn()
-            samples[key].append(timer.region(fn, steps) / steps)
-    ref = outs[0].clone()
-    write_all(torch, outs, lambda o: df.fold_ranks(o, stacked2))
-    same = all_equal(torch, outs, ref)
-    del stacked2
-    res = {"steps_per_region": steps, "regions_each": 3, "outputs_equal": same,
-           "note": "regions of one arena and of two alternating arenas, interleaved; outputs rotate"}
-    for key, v in samples.items():
-        ms = statistics.median(v)
-        res[key] = {"ms_per_step": round(ms, 6), "GBps": round(bytes_per_step / (ms * 1e-3) / 1e9, 2)}
-    log("one arena %.1f GB/s, two alternating arenas %.1f GB/s (interleaved regions; outputs equal: %s)"
-        % (res["one_arena"]["GBps"], res["two_arenas"]["GBps"], same))
-    return res
-
 
 def kernel_name(df, torch, dev, out, stacked, W, n, scaled) -> str:
     """Name of the kernel instance the default launch uses (from the host plan)."""
@@ -1065,12 +1066,13 @@ def bench_one_shot(torch, df, dev, shot, xa, xb):
 
 
 def sweep(args, torch, df, dev):
-    """Launch-geometry sweep of the headline fold, outputs rotating (all
-    results bit-checked against the default launch's output)."""
+    """Launch-geometry sweep of the headline fold, arena copies and outputs
+    rotating (all results bit-checked against the default launch's output)."""
     host, stacked, out, W, n, _ = make_workload("w8", torch, dev)
     timer = Timer(torch, torch.cuda.current_stream(dev))
     df.fold_ranks(out, stacked)
     ref = out.clone()
+    arenas = arena_set(torch, stacked, WORKLOADS["w8"][5])
     outs = output_set(torch, out)
     bytes_per_step = (W + 1) * n * 4
     configs = [(df.PATH_ROWS, df.POLICY_STREAM, 64 * W, 1, grid) for grid in (0, 512, 1024, 2048, 4096)]
@@ -1084,15 +1086,20 @@ def sweep(args, torch, df, dev):
         for c in configs:
             path, policy, block, unroll, grid = c
 
-            def call(o):
-                df.fold_ranks_ex(o, stacked, path=path, block=block, grid=grid, unroll=unroll,
+            def call(o, a):
+                df.fold_ranks_ex(o, a, path=path, block=block, grid=grid, unroll=unroll,
                                  policy=policy)
-            step = rotating(outs, call)
+            state = [0]
+
+            def step():
+                i = state[0]
+                state[0] += 1
+                call(outs[i % len(outs)], arenas[i % len(arenas)])
             for _ in range(3):
                 step()
             samples[c].append(timer.region(step, 20) / 20)
             if rnd == 0:
-                write_all(torch, outs, call)
+                write_all(torch, outs, lambda o: [call(o, a) for a in arenas])
                 if not all_equal(torch, outs, ref):
                     raise AssertionError("sweep configuration %s changed the bits" % (c,))
     rows = []
@@ -1326,8 +1333,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-owner-shards", dest="owner_shards", action="store_false",
                     help="skip the owner-shard folds of the w16 workload (profiling runs that "
                          "summarize the whole fold's kernel)")
-    ap.add_argument("--no-alternate", dest="alternate", action="store_false",
-                    help="skip the two-arena control run")
+    ap.add_argument("--no-controls", "--no-alternate", dest="controls", action="store_false",
+                    help="skip the interleaved cache controls (one arena, every operand reused)")
     ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
                     help="skip the library streaming probes (the attainable ceiling)")
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",

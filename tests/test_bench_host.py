@@ -57,9 +57,43 @@ def test_output_set_spans_twice_the_memory_side_cache():
         assert all(o.shape == out.shape and o.dtype == out.dtype for o in outs)
 
 
-def test_rotating_step_takes_the_buffers_in_turn():
+def test_fold_step_takes_arenas_and_outputs_in_turn():
     seen = []
-    step = bench.rotating(["a", "b", "c"], seen.append)
-    for _ in range(7):
+
+    class Lib:
+        def fold_ranks(self, o, s):
+            seen.append(("plain", o, s))
+
+        def fold_ranks_scaled(self, o, s, inv_w):
+            seen.append((inv_w, o, s))
+
+    step = bench.fold_step(Lib(), ["o0", "o1", "o2"], ["a0", "a1"], None)
+    for _ in range(6):
         step()
-    assert seen == ["a", "b", "c", "a", "b", "c", "a"]
+    assert seen == [("plain", "o0", "a0"), ("plain", "o1", "a1"), ("plain", "o2", "a0"),
+                    ("plain", "o0", "a1"), ("plain", "o1", "a0"), ("plain", "o2", "a1")]
+    seen.clear()
+    step = bench.fold_step(Lib(), ["o0"], ["a0"], 0.25)
+    step()
+    assert seen == [(0.25, "o0", "a0")]
+
+
+def test_arena_set_copies_keep_the_phase_and_the_contents(monkeypatch):
+    import torch
+    monkeypatch.setattr(bench, "MEMORY_SIDE_CACHE_BYTES", 1024)
+    W, n, offset = 8, 100, 1
+    alloc = torch.empty(W * n + offset, dtype=torch.float32)
+    stacked = alloc[offset:].view(W, n)
+    stacked.copy_(torch.arange(W * n, dtype=torch.float32).view(W, n))
+    copies = bench.arena_set(torch, stacked, offset)
+    # 1 + ceil(4 * 1024 / 3200) copies: at least 4x the cache of other copies between reuses
+    assert len(copies) == 3 and copies[0] is stacked
+    for c in copies[1:]:
+        assert c.shape == (W, n) and c.data_ptr() != stacked.data_ptr()
+        assert c.data_ptr() % 16 == stacked.data_ptr() % 16
+        assert torch.equal(c, stacked)
+    monkeypatch.setattr(bench, "MEMORY_SIDE_CACHE_BYTES", 256 << 20)
+    meta = torch.empty((8, 1 << 24), dtype=torch.float32, device="meta")
+    assert len(bench.arena_set(torch, meta, 0)) == 3      # W=8 x 2^24: 512 MiB per copy
+    meta = torch.empty((4, 100_000_000), dtype=torch.float32, device="meta")
+    assert len(bench.arena_set(torch, meta, 0)) == 2      # W=4 x 1e8: 1.6 GB per copy
