@@ -31,8 +31,12 @@ constexpr int kWideSlots = 16;     // slots per pass of the wide row body (W > k
 // keep the sixteen-wave shape and take runs of kWideShiftedGroup tiles per
 // XCD: +0.4% to +2.1% over plain round-robin at six arenas of W = 17..48,
 // lengths 5e6 to 1.2e7, one to three elements off (6 interleaved rounds,
-// outputs rotating past the memory-side cache, bit-checked), never a loss;
-// runs of 8 gained +0.3% to +2.1%, of 32 -0.4% to +2.0%.
+// outputs rotating past the memory-side cache, one arena, bit-checked);
+// runs of 8 gained +0.3% to +2.1%, of 32 -0.4% to +2.0%.  With copies of
+// the arena rotating as well the same six read -1.6% to +2.2% (+0.4% on
+// average), so the rule rests as much on the traffic: the shared boundary
+// lines of the 4 KiB runs are fetched once per XCD run instead of twice
+// (W=32 x 8,000,001 at base+1: 1.030x -> 1.012x the algorithmic bytes).
 constexpr int kWideWaves = 16, kWideKiB = 4;
 constexpr int kWideAlignedWaves = 8, kWideAlignedKiB = 1;
 constexpr int kWideShiftedGroup = 16;
