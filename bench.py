@@ -228,10 +228,12 @@ def fold_step(df, outs, arenas, inv_w):
     return step
 
 
-def write_all(torch, outs, call):
-    """call(o) once for every o in outs, then wait: every buffer holds a result."""
-    for o in outs:
-        call(o)
+def fill_outputs(torch, df, outs, arenas, inv_w):
+    """Output k := the fold of arena copy k mod A, then wait: with at least as
+    many outputs as copies, the bit checks of the outputs cover every copy."""
+    call = fold_call(df, inv_w)
+    for k, o in enumerate(outs):
+        call(o, arenas[k % len(arenas)])
     torch.cuda.synchronize()
 
 
@@ -327,8 +329,7 @@ def bench_fold(args, torch, df, dev):
     sustained = bench_sustained(args, timer, step, bytes_per_step)
     controls = bench_cache_controls(args, df, timer, outs, arenas, inv_w, bytes_per_step) \
         if args.controls else None
-    call = fold_call(df, inv_w)
-    write_all(torch, outs, lambda o: [call(o, a) for a in arenas])
+    fill_outputs(torch, df, outs, arenas, inv_w)
 
     singles = bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step) \
         if args.singles > 0 else None
@@ -399,8 +400,7 @@ def bench_secondary(args, torch, df, dev, name):
     sustained = bench_sustained(args, timer, step, bytes_per_step)
     controls = bench_cache_controls(args, df, timer, outs, arenas, inv_w, bytes_per_step) \
         if args.controls else None
-    call = fold_call(df, inv_w)
-    write_all(torch, outs, lambda o: [call(o, a) for a in arenas])
+    fill_outputs(torch, df, outs, arenas, inv_w)
     exact = oracle_check(host, inv_w, outs)
     log("%s: %.4f ms per step, %.1f GB/s (%.1f%% of peak); kernel-only average %.4f ms; bit-exact vs "
         "the oracle: %s" % (name, ms, gbs, 100 * gbs / HBM_PEAK_GBS, statistics.mean(kern), exact))
@@ -1099,7 +1099,9 @@ def sweep(args, torch, df, dev):
                 step()
             samples[c].append(timer.region(step, 20) / 20)
             if rnd == 0:
-                write_all(torch, outs, lambda o: [call(o, a) for a in arenas])
+                for k, o in enumerate(outs):
+                    call(o, arenas[k % len(arenas)])
+                torch.cuda.synchronize()
                 if not all_equal(torch, outs, ref):
                     raise AssertionError("sweep configuration %s changed the bits" % (c,))
     rows = []

@@ -97,3 +97,20 @@ def test_arena_set_copies_keep_the_phase_and_the_contents(monkeypatch):
     assert len(bench.arena_set(torch, meta, 0)) == 3      # W=8 x 2^24: 512 MiB per copy
     meta = torch.empty((4, 100_000_000), dtype=torch.float32, device="meta")
     assert len(bench.arena_set(torch, meta, 0)) == 2      # W=4 x 1e8: 1.6 GB per copy
+
+
+def test_fill_outputs_takes_every_arena_copy(monkeypatch):
+    seen = []
+
+    class Lib:
+        def fold_ranks(self, o, s):
+            seen.append((o, s))
+
+    class Torch:
+        class cuda:
+            @staticmethod
+            def synchronize():
+                seen.append("sync")
+
+    bench.fill_outputs(Torch, Lib(), ["o0", "o1", "o2", "o3", "o4"], ["a0", "a1", "a2"], None)
+    assert seen == [("o0", "a0"), ("o1", "a1"), ("o2", "a2"), ("o3", "a0"), ("o4", "a1"), "sync"]
