@@ -19,6 +19,14 @@ constexpr int kStreamBlock = 512;  // largest default workgroup of the bandwidth
 constexpr int kChunk = 8;          // slots loaded per batch when W is a runtime value
 constexpr int kMaxRowsW = 16;      // widest fold the LDS row body takes (one wave per slot)
 constexpr int kWideSlots = 16;     // slots per pass of the wide row body (W > kMaxRowsW)
+
+// The measured notes below compare shapes within one interleaved sweep.  Unless
+// a note says otherwise, those sweeps folded one arena into one output over
+// and over; the memory-side cache then serves part of the traffic, so their
+// absolute rates run 2-5% above what the same fold reaches with its operands
+// out of that cache, while the comparisons they support were rechecked with
+// the operands rotating.
+
 // Shapes of a pass of the wide row body: 16 waves x 1 slot x 4 KiB, or, when
 // every slot shares out's 16-byte phase, 8 waves x 2 slots x 1 KiB (measured
 // on MI355X at W = 24..64: 2.6-21.5% faster co-aligned, 2.7-5.5% slower with
