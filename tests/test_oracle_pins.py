@@ -110,8 +110,12 @@ def _same_bits(got, want):
 def _double_path(stacked):
     s = np.asarray(stacked, dtype=np.float32)
     acc = s[0].astype(np.float64)
-    for r in range(1, s.shape[0]):
-        acc = (acc + s[r].astype(np.float64)).astype(np.float32).astype(np.float64)
+    # A double sum beyond the binary32 range rounds to +-inf in the cast: that is
+    # the rounding each step of the chain must take, so numpy's overflow warning
+    # is expected here and silenced.
+    with np.errstate(over="ignore"):
+        for r in range(1, s.shape[0]):
+            acc = (acc + s[r].astype(np.float64)).astype(np.float32).astype(np.float64)
     return acc.astype(np.float32)
 
 
