@@ -333,7 +333,7 @@ def bench_fold(args, torch, df, dev):
 
     singles = bench_singles(args, torch, df, dev, timer, out, stacked, inv_w, bytes_per_step) \
         if args.singles > 0 else None
-    ceiling = bench_ceiling(args, torch, dev, timer, stacked, out) if args.ceiling else None
+    ceiling = bench_ceiling(args, torch, dev, timer, arenas, outs) if args.ceiling else None
     attainable = ceiling["attainable_GBps"] if ceiling else None
 
     result = {
@@ -525,40 +525,49 @@ def settle(timer, step, target_ms=100.0):
     timer.torch.cuda.synchronize()
 
 
-def bench_ceiling(args, torch, dev, timer, stacked, out):
+def bench_ceiling(args, torch, dev, timer, arenas, outs):
     """What plain streaming reaches on this machine with library kernels: torch
-    reductions over the slot axis of the same arena (the fold's byte mix, W
-    reads to one write: amax carries no additions, sum other ones), a device
-    copy of the whole arena (1:1), a fill of it (writes only) and a sum of it
-    to one value (reads only).  Each rate counts the bytes the operation must
-    move, over back-to-back calls timed with events.  attainable_GBps is the
-    best of them."""
-    W, n = stacked.shape
+    reductions over the slot axis of the arena (the fold's byte mix, W reads
+    to one write: amax carries no additions, sum other ones), a device copy of
+    the whole arena (1:1), a fill of it (writes only) and a sum of it to one
+    value (reads only).  Like the fold's steps, call i takes arena copy
+    i mod A, a reduction output i mod R (R buffers of the fold's output's size,
+    not the fold's own outputs, which the oracle check reads afterwards) and
+    scratch buffer i mod 2 (two arena-sized buffers, twice the memory-side
+    cache together), so no probe finds its operands in that cache either.  Each rate counts the bytes the operation
+    must move, over back-to-back calls timed with events.  attainable_GBps is
+    the best of them."""
+    W, n = arenas[0].shape
     arena = W * n * 4
-    tmp = torch.empty_like(out)
-    scratch = torch.empty_like(stacked)
+    scratch = [torch.empty_like(arenas[0]) for _ in range(2)]
+    tmps = [torch.empty_like(o) for o in outs]
+    A, R = len(arenas), len(tmps)
     probes = {
-        "amax_over_slots": (lambda: torch.amax(stacked, dim=0, out=tmp), arena + n * 4),
-        "sum_over_slots": (lambda: torch.sum(stacked, dim=0, out=tmp), arena + n * 4),
-        "copy_arena": (lambda: scratch.copy_(stacked), 2 * arena),
-        "fill_arena": (lambda: scratch.fill_(1.0), arena),
-        "sum_arena_to_scalar": (lambda: stacked.sum(), arena),
+        "amax_over_slots": (lambda i: torch.amax(arenas[i % A], dim=0, out=tmps[i % R]), arena + n * 4),
+        "sum_over_slots": (lambda i: torch.sum(arenas[i % A], dim=0, out=tmps[i % R]), arena + n * 4),
+        "copy_arena": (lambda i: scratch[i % 2].copy_(arenas[i % A]), 2 * arena),
+        "fill_arena": (lambda i: scratch[i % 2].fill_(1.0), arena),
+        "sum_arena_to_scalar": (lambda i: arenas[i % A].sum(), arena),
     }
-    reps = max(5, min(args.steps, 50))
+    reps = max(6, min(args.steps, 48))
     res = {}
     for key, (fn, moved) in probes.items():
+        state = [0]
+
+        def step():
+            fn(state[0])
+            state[0] += 1
         for _ in range(3):
-            fn()
-        ms = timer.region(fn, reps) / reps
+            step()
+        ms = timer.region(step, reps) / reps
         res[key] = {"ms": round(ms, 6), "bytes": moved, "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
         log("ceiling probe %-20s %.4f ms, %.1f GB/s" % (key, ms, res[key]["GBps"]))
-    del tmp, scratch
+    del scratch, tmps
     torch.cuda.empty_cache()
     best = max(res, key=lambda k: res[k]["GBps"])
     return {"probes": res, "attainable_GBps": res[best]["GBps"], "best_probe": best,
             "note": "library streaming kernels on the headline arena (torch reductions, copy, fill), "
-                    "back-to-back, bytes each operation must move"}
-
+                    "back-to-back, operands rotating as the fold's do, bytes each operation must move"}
 
 def device_info(torch, dev):
     """What the device reports: CU count, peak memory clock and bus width (HIP
